@@ -1,0 +1,135 @@
+/*
+ * fcshard.h - C ABI of the per-GPU shard GEMMs of a 3D-parallel FC layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation. One fully connected layer's matrix multiply is split over a
+ * Gx x Gy x Gz virtual grid of GPUs with Agarwal's 3D parallel matrix
+ * multiplication (sciencestack.ai/paper/2502.08145, Figure 1). After the
+ * collectives that move shards around (pith.science/paper/2502.08145, "What
+ * carries the argument": weight sharded along Z, all-gather, reduce-scatter,
+ * all-reduce), each GPU runs three local bf16 matrix products on its shard:
+ *
+ *   forward          Y  = X . W      X: M x K, W: K x N, Y: M x N
+ *   backward-data    dX = dY . W^T   dY: M x N, dX: M x K
+ *   backward-weight  dW = X^T . dY   dW: K x N (the local, un-reduced block)
+ *
+ * M counts tokens of the shard, K input features, N output features. Inputs
+ * are bf16 (mlsanity.com/paper/2502.08145, Abstract: bf16 training); products
+ * are accumulated in fp32 and the output is rounded to bf16 (nearest-even) or
+ * stored as fp32. Automated kernel tuning is one of the pages' named
+ * optimisations (sciencestack.ai/paper/2502.08145, TL;DR); fc_tune is this
+ * library's per-shape version of it.
+ *
+ * Layout. Every matrix is tightly packed (leading dimension = its column
+ * count in its storage order). X and W take a storage order; dY, Y, dX and dW
+ * are always row-major. A PyTorch nn.Linear weight (N x K, row-major) is W in
+ * FC_COL_MAJOR.
+ *
+ * Ownership. All data pointers are DEVICE pointers owned by the caller. The
+ * library owns only its plan cache and one workspace per device, which grow
+ * only inside fc_tune / fc_set_plan and are freed by fc_release.
+ *
+ * Hot calls (fc_fwd, fc_bwd_data, fc_bwd_weight) never allocate and never
+ * synchronize: they validate, enqueue kernels on `stream` (a hipStream_t;
+ * NULL is the null stream) and return. A shape that was never tuned runs a
+ * default plan that needs no workspace. Errors are returned, never thrown;
+ * the library never aborts. Device faults surface at the caller's next
+ * synchronization, as for any asynchronous HIP call.
+ *
+ * Threading: the plan cache is guarded by a mutex; hot calls are re-entrant.
+ * Determinism: the same plan on the same inputs gives bitwise-identical
+ * output (split-K partials are summed in a fixed order, no atomics).
+ */
+#ifndef FCSHARD_H
+#define FCSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FC_OK = 0,
+    FC_E_INVALID = 1,     /* NULL pointer, dimension < 1, bad enum, misaligned or overlapping output */
+    FC_E_UNSUPPORTED = 2, /* current device is not gfx950, or plan id not applicable */
+    FC_E_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    FC_E_NOMEM = 4        /* workspace or tuning buffers could not be allocated */
+} fc_status;
+
+/* storage order of a LOGICAL matrix */
+typedef enum { FC_ROW_MAJOR = 0, FC_COL_MAJOR = 1 } fc_order;
+
+/* output element type */
+typedef enum { FC_OUT_BF16 = 0, FC_OUT_F32 = 1 } fc_out_dtype;
+
+/* the three products, for the plan-control calls */
+typedef enum { FC_OP_FWD = 0, FC_OP_BWD_DATA = 1, FC_OP_BWD_WEIGHT = 2 } fc_op;
+
+/*
+ * Y[M x N] = X[M x K] . W[K x N]   (forward; reduction over K).
+ * X: bf16, x_order; W: bf16, w_order; Y: row-major, y_dtype.
+ * Y must not overlap X or W. Base pointers need 2-byte (bf16) or 4-byte
+ * (fp32) alignment; 16-byte-aligned bases with M, K, N multiples of 8 take
+ * the vectorized kernels.
+ */
+fc_status fc_fwd(const void* X, fc_order x_order, const void* W, fc_order w_order,
+                 void* Y, fc_out_dtype y_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * dX[M x K] = dY[M x N] . W[K x N]^T   (backward-data; reduction over N).
+ * dY: bf16 row-major; W: bf16, w_order; dX: row-major, dx_dtype.
+ */
+fc_status fc_bwd_data(const void* dY, const void* W, fc_order w_order,
+                      void* dX, fc_out_dtype dx_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * dW[K x N] = X[M x K]^T . dY[M x N]   (backward-weight; reduction over the
+ * M tokens). X: bf16, x_order; dY: bf16 row-major; dW: row-major, dw_dtype.
+ * dW is this GPU's local block; in the full method it would then be
+ * reduce-scattered over Gz.
+ */
+fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY,
+                        void* dW, fc_out_dtype dw_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * Times candidate plans of all three products at (M, K, N, x_order, w_order,
+ * out_dtype) on `stream` and caches the fastest per product. flags: 0 =
+ * quick search, 1 = exhaustive. Allocates temporary buffers and may grow the
+ * workspace; synchronizes `stream`. Plans are kept until fc_release.
+ */
+fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                  fc_out_dtype out_dtype, int flags, void* stream);
+
+/* number of plan ids (plan ids are 0 .. fc_plan_count()-1) */
+int fc_plan_count(void);
+
+/*
+ * Forces plan `plan_id` for one product at one key, as if tuned (grows the
+ * workspace if the plan needs one). FC_E_UNSUPPORTED if the plan does not
+ * apply to this shape (e.g. a vectorized tile on an unaligned shape).
+ * plan_id = -1 removes the cache entry (back to the default plan).
+ */
+fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                      fc_out_dtype out_dtype, int plan_id);
+
+/*
+ * Describes the plan a hot call at this key would run: writes a NUL-terminated
+ * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> ws=<bytes>"
+ * into buf (truncated to len). Returns FC_E_INVALID for bad arguments.
+ */
+fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order,
+                           fc_order w_order, fc_out_dtype out_dtype, char* buf, size_t len);
+
+/* static text for a status; never NULL */
+const char* fc_status_str(fc_status status);
+
+/* frees the library-owned workspaces and clears the plan cache */
+fc_status fc_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCSHARD_H */

@@ -1,0 +1,595 @@
+// C ABI of the shard GEMM library: validation, storage-order resolution,
+// plan space, plan cache, workspace and the per-shape tuner.
+//
+// The three products of one GPU's FC-layer shard (sciencestack.ai/paper/
+// 2502.08145, Figure 1) map onto one GEMM family C = A.B whose operands are
+// either reduction-contiguous (RC) or output-contiguous (OC) in memory:
+//
+//   product          A        B        row/row   row/col   col/row   col/col
+//   forward Y=X.W    X        W        RC,OC     RC,RC     OC,OC     OC,RC
+//   bwd-data dX      dY       W^T      RC,RC     RC,OC     RC,RC     RC,OC
+//   bwd-weight dW    X^T      dY       OC,OC     OC,OC     RC,OC     RC,OC
+//
+// (orders are x_order/w_order). A plan chooses the block tile, a split of the
+// reduction (fp32 partials summed in a fixed order) and whether OC operands
+// are first copied to RC form in the workspace (the tuner's transpose-vs-copy
+// choice, after the pages' automated kernel tuning: sciencestack.ai/paper/
+// 2502.08145, TL;DR).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/fcshard.h"
+#include "fcshard_internal.h"
+
+namespace fcs {
+namespace {
+
+constexpr int kSplits[] = {1, 2, 4};
+constexpr int kNumSplits = 3;
+constexpr int kNumCopy = 4;  // bit 0: copy A to RC, bit 1: copy B to RC
+constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy;
+constexpr int kMaxDevices = 64;
+
+struct Plan {
+    int tile;
+    int split;  // number of reduction slices requested
+    int copy;   // bit mask
+};
+
+Plan decode_plan(int id) {
+    Plan p;
+    p.tile = id % kNumTiles;
+    p.split = kSplits[(id / kNumTiles) % kNumSplits];
+    p.copy = id / (kNumTiles * kNumSplits);
+    return p;
+}
+
+// One GEMM in kernel terms, resolved from an ABI call.
+struct Problem {
+    const uint16_t* A;
+    const uint16_t* B;
+    void* C;
+    bool a_oc, b_oc, out_f32;
+    int64_t M, N, K;  // output rows, output cols, reduction
+};
+
+bool problem_aligned(const Problem& p) {
+    return p.M % 8 == 0 && p.N % 8 == 0 && p.K % 8 == 0 && (uintptr_t)p.A % 16 == 0 &&
+           (uintptr_t)p.B % 16 == 0 && (uintptr_t)p.C % 16 == 0;
+}
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Effective reduction slicing: slice length is a multiple of 64.
+void split_geometry(int64_t K, int split, int64_t* k_split, int* slices) {
+    if (split <= 1) {
+        *k_split = round_up(K, 64);
+        *slices = 1;
+        return;
+    }
+    int64_t ks = round_up((K + split - 1) / split, 64);
+    *k_split = ks;
+    *slices = (int)((K + ks - 1) / ks);
+}
+
+struct WsLayout {
+    int64_t a_off, b_off, p_off, total;
+};
+
+WsLayout ws_layout(const Problem& p, const Plan& pl) {
+    WsLayout w{0, 0, 0, 0};
+    int64_t off = 0;
+    if ((pl.copy & 1) && p.a_oc) {
+        w.a_off = off;
+        off += round_up(p.M * p.K * 2, 256);
+    }
+    if ((pl.copy & 2) && p.b_oc) {
+        w.b_off = off;
+        off += round_up(p.N * p.K * 2, 256);
+    }
+    int64_t ks;
+    int slices;
+    split_geometry(p.K, pl.split, &ks, &slices);
+    if (slices > 1) {
+        w.p_off = off;
+        off += round_up((int64_t)slices * p.M * p.N * 4, 256);
+    }
+    w.total = off;
+    return w;
+}
+
+// Is the plan meaningful for this problem?
+bool plan_applies(const Problem& p, const Plan& pl) {
+    if ((pl.copy & 1) && !p.a_oc) return false;
+    if ((pl.copy & 2) && !p.b_oc) return false;
+    const bool aligned_after_copy = p.M % 8 == 0 && p.N % 8 == 0 && p.K % 8 == 0 &&
+                                    (uintptr_t)p.C % 16 == 0 &&
+                                    ((pl.copy & 1) || (uintptr_t)p.A % 16 == 0) &&
+                                    ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
+    if (!aligned_after_copy && pl.tile != kUnalignedTile) return false;
+    if (pl.split > 1) {
+        int64_t ks;
+        int slices;
+        split_geometry(p.K, pl.split, &ks, &slices);
+        if (slices < 2) return false;
+    }
+    return true;
+}
+
+// ----------------------------------------------------------------- state
+
+struct Key {
+    int dev, op;
+    int64_t M, K, N;
+    int xo, wo, f32;
+    bool operator<(const Key& o) const {
+        return std::tie(dev, op, M, K, N, xo, wo, f32) < std::tie(o.dev, o.op, o.M, o.K, o.N, o.xo, o.wo, o.f32);
+    }
+};
+
+struct DevState {
+    int checked = 0;  // 0 unknown, 1 gfx950, -1 other
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<Key, int> g_plans;
+DevState g_dev[kMaxDevices];
+
+bool log_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = std::getenv("FC_LOG");
+        v = (e && *e && *e != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+fc_status check_device(int* dev_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FC_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FC_E_UNSUPPORTED;
+    *dev_out = dev;
+    DevState& d = g_dev[dev];
+    if (d.checked == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FC_E_HIP;
+        d.checked = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    }
+    return d.checked == 1 ? FC_OK : FC_E_UNSUPPORTED;
+}
+
+// default plan: no workspace, no split; the largest tile that still gives
+// every CU work
+int default_plan(const Problem& p) {
+    if (!problem_aligned(p)) return kUnalignedTile;
+    int cus = 256;
+    for (int t = 0; t < kNumTiles; ++t) {
+        const int64_t tiles = ((p.M + kTiles[t].bm - 1) / kTiles[t].bm) * ((p.N + kTiles[t].bn - 1) / kTiles[t].bn);
+        if (tiles >= cus) return t;
+    }
+    return kUnalignedTile;  // 128x128 (also valid aligned)
+}
+
+// ------------------------------------------------------------- execution
+
+hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) {
+    Problem p = p0;
+    const WsLayout w = ws_layout(p0, pl);
+    char* base = static_cast<char*>(ws);
+    int64_t lda = p.a_oc ? p.M : p.K;
+    int64_t ldb = p.b_oc ? p.N : p.K;
+    hipError_t e;
+    if ((pl.copy & 1) && p.a_oc) {  // A stored K x M -> M x K
+        uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.a_off);
+        if ((e = launch_transpose_bf16(p.A, dst, p.K, p.M, s)) != hipSuccess) return e;
+        p.A = dst;
+        p.a_oc = false;
+        lda = p.K;
+    }
+    if ((pl.copy & 2) && p.b_oc) {  // B stored K x N -> N x K
+        uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.b_off);
+        if ((e = launch_transpose_bf16(p.B, dst, p.K, p.N, s)) != hipSuccess) return e;
+        p.B = dst;
+        p.b_oc = false;
+        ldb = p.K;
+    }
+    int64_t ks;
+    int slices;
+    split_geometry(p.K, pl.split, &ks, &slices);
+    const bool aligned = problem_aligned(p);
+    GemmArgs g;
+    g.A = p.A;
+    g.B = p.B;
+    g.M = p.M;
+    g.N = p.N;
+    g.K = p.K;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.k_split = ks;
+    g.splits = slices;
+    if (slices > 1) {
+        float* part = reinterpret_cast<float*>(base + w.p_off);
+        g.C = part;
+        g.c_split_stride = p.M * p.N;
+        if ((e = launch_gemm(pl.tile, p.a_oc, p.b_oc, true, true && aligned, g, s)) != hipSuccess) return e;
+        return launch_splitk_reduce(part, p.C, p.out_f32, p.M * p.N, slices, p.M * p.N, s);
+    }
+    g.C = p.C;
+    g.c_split_stride = 0;
+    return launch_gemm(pl.tile, p.a_oc, p.b_oc, p.out_f32, aligned, g, s);
+}
+
+// ------------------------------------------------------------ validation
+
+bool bad_order(int o) { return o != FC_ROW_MAJOR && o != FC_COL_MAJOR; }
+bool bad_dtype(int d) { return d != FC_OUT_BF16 && d != FC_OUT_F32; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)abytes;
+    const uintptr_t b0 = (uintptr_t)b, b1 = b0 + (uintptr_t)bbytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// Build the kernel-terms problem of one product (see the table at the top).
+fc_status resolve(int op, const void* P, int p_order, const void* Q, int q_order, void* out, int dtype,
+                  int64_t M, int64_t K, int64_t N, Problem* pr) {
+    if (op < 0 || op > 2) return FC_E_INVALID;
+    if (M < 1 || K < 1 || N < 1) return FC_E_INVALID;
+    if (bad_order(p_order) || bad_order(q_order) || bad_dtype(dtype)) return FC_E_INVALID;
+    if (M > (int64_t)1 << 31 || K > (int64_t)1 << 31 || N > (int64_t)1 << 31) return FC_E_INVALID;
+    Problem p;
+    p.out_f32 = dtype == FC_OUT_F32;
+    p.A = static_cast<const uint16_t*>(P);
+    p.B = static_cast<const uint16_t*>(Q);
+    p.C = out;
+    int64_t pbytes, qbytes, obytes;
+    const int64_t esz = p.out_f32 ? 4 : 2;
+    if (op == FC_OP_FWD) {  // P = X (M x K), Q = W (K x N)
+        p.M = M, p.N = N, p.K = K;
+        p.a_oc = p_order == FC_COL_MAJOR;
+        p.b_oc = q_order == FC_ROW_MAJOR;
+        pbytes = M * K * 2, qbytes = K * N * 2, obytes = M * N * esz;
+    } else if (op == FC_OP_BWD_DATA) {  // P = dY (M x N, row-major), Q = W (K x N)
+        p.M = M, p.N = K, p.K = N;
+        p.a_oc = false;
+        p.b_oc = q_order == FC_COL_MAJOR;
+        pbytes = M * N * 2, qbytes = K * N * 2, obytes = M * K * esz;
+    } else {  // P = X (M x K), Q = dY (M x N, row-major)
+        p.M = K, p.N = N, p.K = M;
+        p.a_oc = p_order == FC_ROW_MAJOR;
+        p.b_oc = true;
+        pbytes = M * K * 2, qbytes = M * N * 2, obytes = K * N * esz;
+    }
+    if (P != nullptr || Q != nullptr || out != nullptr) {
+        if (!P || !Q || !out) return FC_E_INVALID;
+        if ((uintptr_t)P % 2 || (uintptr_t)Q % 2 || (uintptr_t)out % esz) return FC_E_INVALID;
+        if (overlaps(out, obytes, P, pbytes) || overlaps(out, obytes, Q, qbytes)) return FC_E_INVALID;
+    }
+    *pr = p;
+    return FC_OK;
+}
+
+Key make_key(int dev, int op, int64_t M, int64_t K, int64_t N, int xo, int wo, int dtype) {
+    // normalize the orders the product does not read
+    if (op == FC_OP_BWD_DATA) xo = 0;
+    if (op == FC_OP_BWD_WEIGHT) wo = 0;
+    return Key{dev, op, M, K, N, xo, wo, dtype};
+}
+
+fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_order, void* out, int dtype,
+                   int64_t M, int64_t K, int64_t N, void* stream, int xo, int wo) {
+    if (!P || !Q || !out) return FC_E_INVALID;
+    Problem p;
+    fc_status st = resolve(op, P, p_order, Q, q_order, out, dtype, M, K, N, &p);
+    if (st != FC_OK) return st;
+    int dev;
+    Plan pl;
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if ((st = check_device(&dev)) != FC_OK) return st;
+        int id = -1;
+        auto it = g_plans.find(make_key(dev, op, M, K, N, xo, wo, dtype));
+        if (it != g_plans.end()) id = it->second;
+        if (id >= 0) {
+            pl = decode_plan(id);
+            // a plan that no longer applies (alignment) or lacks workspace falls back
+            if (!plan_applies(p, pl) || ws_layout(p, pl).total > g_dev[dev].ws_bytes) id = -1;
+        }
+        if (id < 0) pl = decode_plan(default_plan(p));
+        ws = g_dev[dev].ws;
+    }
+    return run_plan(p, pl, ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
+}
+
+fc_status grow_workspace(int dev, int64_t bytes) {
+    DevState& d = g_dev[dev];
+    if (bytes <= d.ws_bytes) return FC_OK;
+    if (hipDeviceSynchronize() != hipSuccess) return FC_E_HIP;  // old workspace may be in use
+    if (d.ws) hipFree(d.ws);
+    d.ws = nullptr;
+    d.ws_bytes = 0;
+    if (hipMalloc(&d.ws, (size_t)bytes) != hipSuccess) {
+        d.ws = nullptr;
+        (void)hipGetLastError();
+        return FC_E_NOMEM;
+    }
+    d.ws_bytes = bytes;
+    return FC_OK;
+}
+
+std::string describe(const Problem& p, int id, int64_t ws_have) {
+    const Plan pl = decode_plan(id);
+    Problem q = p;
+    if ((pl.copy & 1) && q.a_oc) q.a_oc = false, q.A = nullptr;
+    if ((pl.copy & 2) && q.b_oc) q.b_oc = false, q.B = nullptr;
+    int64_t ks;
+    int slices;
+    split_geometry(p.K, pl.split, &ks, &slices);
+    const bool aligned = q.M % 8 == 0 && q.N % 8 == 0 && q.K % 8 == 0 &&
+                         (uintptr_t)p.C % 16 == 0 && (q.A == nullptr || (uintptr_t)q.A % 16 == 0) &&
+                         (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
+    const char* kname = gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc,
+                                         slices > 1 ? true : p.out_f32, aligned);
+    char buf[512];
+    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname,
+                  kTiles[aligned ? pl.tile : kUnalignedTile].name, slices, pl.copy,
+                  (long long)ws_layout(p, pl).total);
+    (void)ws_have;
+    return buf;
+}
+
+// --------------------------------------------------------------- tuning
+
+struct TuneBuffers {
+    void* X = nullptr;
+    void* W = nullptr;
+    void* dY = nullptr;
+    void* out = nullptr;
+    ~TuneBuffers() {
+        if (X) hipFree(X);
+        if (W) hipFree(W);
+        if (dY) hipFree(dY);
+        if (out) hipFree(out);
+    }
+};
+
+float time_plan(const Problem& p, const Plan& pl, void* ws, hipStream_t s, int warm, int reps, hipEvent_t* ev,
+                bool* ok) {
+    *ok = true;
+    for (int i = 0; i < warm; ++i)
+        if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
+    std::vector<float> t;
+    for (int i = 0; i < reps && *ok; ++i) {
+        hipEventRecord(ev[0], s);
+        if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
+        hipEventRecord(ev[1], s);
+        if (hipEventSynchronize(ev[1]) != hipSuccess) *ok = false;
+        float ms = 0;
+        hipEventElapsedTime(&ms, ev[0], ev[1]);
+        t.push_back(ms);
+    }
+    if (!*ok || t.empty()) return 1e30f;
+    std::sort(t.begin(), t.end());
+    return t[t.size() / 2];
+}
+
+}  // namespace
+}  // namespace fcs
+
+using namespace fcs;
+
+extern "C" {
+
+fc_status fc_fwd(const void* X, fc_order x_order, const void* W, fc_order w_order, void* Y, fc_out_dtype y_dtype,
+                 int64_t M, int64_t K, int64_t N, void* stream) {
+    return hot_call(FC_OP_FWD, X, x_order, W, w_order, Y, y_dtype, M, K, N, stream, x_order, w_order);
+}
+
+fc_status fc_bwd_data(const void* dY, const void* W, fc_order w_order, void* dX, fc_out_dtype dx_dtype, int64_t M,
+                      int64_t K, int64_t N, void* stream) {
+    return hot_call(FC_OP_BWD_DATA, dY, FC_ROW_MAJOR, W, w_order, dX, dx_dtype, M, K, N, stream, FC_ROW_MAJOR,
+                    w_order);
+}
+
+fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY, void* dW, fc_out_dtype dw_dtype,
+                        int64_t M, int64_t K, int64_t N, void* stream) {
+    return hot_call(FC_OP_BWD_WEIGHT, X, x_order, dY, FC_ROW_MAJOR, dW, dw_dtype, M, K, N, stream, x_order,
+                    FC_ROW_MAJOR);
+}
+
+int fc_plan_count(void) { return kNumPlans; }
+
+fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                      fc_out_dtype out_dtype, int plan_id) {
+    if (bad_order(x_order) || bad_order(w_order) || bad_dtype(out_dtype)) return FC_E_INVALID;
+    if (plan_id < -1 || plan_id >= kNumPlans) return FC_E_INVALID;
+    int p_order = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : x_order;
+    int q_order = op == FC_OP_BWD_WEIGHT ? FC_ROW_MAJOR : w_order;
+    Problem p;
+    fc_status st = resolve(op, nullptr, p_order, nullptr, q_order, nullptr, out_dtype, M, K, N, &p);
+    if (st != FC_OK) return st;
+    std::lock_guard<std::mutex> lk(g_mu);
+    int dev;
+    if ((st = check_device(&dev)) != FC_OK) return st;
+    const Key key = make_key(dev, op, M, K, N, x_order, w_order, out_dtype);
+    if (plan_id < 0) {
+        g_plans.erase(key);
+        return FC_OK;
+    }
+    // alignment of pointers is not known here: judge the shape only
+    p.A = p.B = nullptr;
+    p.C = nullptr;
+    const Plan pl = decode_plan(plan_id);
+    if (!plan_applies(p, pl)) return FC_E_UNSUPPORTED;
+    if ((st = grow_workspace(dev, ws_layout(p, pl).total)) != FC_OK) return st;
+    g_plans[key] = plan_id;
+    return FC_OK;
+}
+
+fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                           fc_out_dtype out_dtype, char* buf, size_t len) {
+    if (!buf || len == 0) return FC_E_INVALID;
+    if (bad_order(x_order) || bad_order(w_order) || bad_dtype(out_dtype)) return FC_E_INVALID;
+    int p_order = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : x_order;
+    int q_order = op == FC_OP_BWD_WEIGHT ? FC_ROW_MAJOR : w_order;
+    Problem p;
+    fc_status st = resolve(op, nullptr, p_order, nullptr, q_order, nullptr, out_dtype, M, K, N, &p);
+    if (st != FC_OK) return st;
+    std::lock_guard<std::mutex> lk(g_mu);
+    int dev;
+    if ((st = check_device(&dev)) != FC_OK) return st;
+    p.A = p.B = nullptr;
+    p.C = nullptr;
+    int id = -1;
+    auto it = g_plans.find(make_key(dev, op, M, K, N, x_order, w_order, out_dtype));
+    if (it != g_plans.end()) id = it->second;
+    if (id >= 0 && ws_layout(p, decode_plan(id)).total > g_dev[dev].ws_bytes) id = -1;
+    if (id < 0) id = default_plan(p);
+    const std::string s = describe(p, id, g_dev[dev].ws_bytes);
+    std::snprintf(buf, len, "%s", s.c_str());
+    return FC_OK;
+}
+
+fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order, fc_out_dtype out_dtype,
+                  int flags, void* stream) {
+    if (bad_order(x_order) || bad_order(w_order) || bad_dtype(out_dtype)) return FC_E_INVALID;
+    if (M < 1 || K < 1 || N < 1) return FC_E_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        fc_status st = check_device(&dev);
+        if (st != FC_OK) return st;
+    }
+    TuneBuffers b;
+    const int64_t esz = out_dtype == FC_OUT_F32 ? 4 : 2;
+    const int64_t out_elems = std::max(M * N, std::max(M * K, K * N));
+    if (hipMalloc(&b.X, M * K * 2) != hipSuccess || hipMalloc(&b.W, K * N * 2) != hipSuccess ||
+        hipMalloc(&b.dY, M * N * 2) != hipSuccess || hipMalloc(&b.out, out_elems * esz) != hipSuccess) {
+        (void)hipGetLastError();
+        return FC_E_NOMEM;
+    }
+    if (launch_fill_bf16((uint16_t*)b.X, M * K, 1u, s) != hipSuccess ||
+        launch_fill_bf16((uint16_t*)b.W, K * N, 2u, s) != hipSuccess ||
+        launch_fill_bf16((uint16_t*)b.dY, M * N, 3u, s) != hipSuccess)
+        return FC_E_HIP;
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) return FC_E_HIP;
+    const bool exhaustive = (flags & 1) != 0;
+    const int warm = exhaustive ? 3 : 2, reps = exhaustive ? 10 : 5;
+    fc_status result = FC_OK;
+
+    for (int op = 0; op < 3; ++op) {
+        const void* P = op == FC_OP_BWD_DATA ? b.dY : b.X;
+        const void* Q = op == FC_OP_FWD ? b.W : (op == FC_OP_BWD_DATA ? b.W : b.dY);
+        const int p_order = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : x_order;
+        const int q_order = op == FC_OP_BWD_WEIGHT ? FC_ROW_MAJOR : w_order;
+        Problem p;
+        fc_status st = resolve(op, P, p_order, Q, q_order, b.out, out_dtype, M, K, N, &p);
+        if (st != FC_OK) {
+            result = st;
+            break;
+        }
+        // candidate plans
+        std::vector<int> cand;
+        int64_t need = 0;
+        for (int id = 0; id < kNumPlans; ++id) {
+            const Plan pl = decode_plan(id);
+            if (!plan_applies(p, pl)) continue;
+            if (!exhaustive && pl.split > 1 && pl.copy != 0) continue;
+            cand.push_back(id);
+            need = std::max(need, ws_layout(p, pl).total);
+        }
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            if (grow_workspace(dev, need) != FC_OK) {
+                // keep only the plans that fit what is there
+                std::vector<int> keep;
+                for (int id : cand)
+                    if (ws_layout(p, decode_plan(id)).total <= g_dev[dev].ws_bytes) keep.push_back(id);
+                cand.swap(keep);
+            }
+        }
+        void* ws = g_dev[dev].ws;
+        int best = -1;
+        float best_ms = 1e30f;
+        std::vector<std::pair<int, float>> times;
+        for (int id : cand) {
+            bool ok;
+            const float ms = time_plan(p, decode_plan(id), ws, s, warm, reps, ev, &ok);
+            if (!ok) {
+                (void)hipGetLastError();
+                continue;
+            }
+            times.push_back({id, ms});
+            if (ms < best_ms) best_ms = ms, best = id;
+        }
+        // tie-break within 1%: no workspace, then no split, then the lower id
+        int pick = best;
+        for (auto& t : times) {
+            if (t.second > best_ms * 1.01f) continue;
+            const Plan a = decode_plan(t.first), c = decode_plan(pick);
+            const int64_t wa = ws_layout(p, a).total, wc = ws_layout(p, c).total;
+            const auto ka = std::make_tuple(wa > 0, a.split > 1, t.first);
+            const auto kc = std::make_tuple(wc > 0, c.split > 1, pick);
+            if (ka < kc) pick = t.first;
+        }
+        if (log_enabled()) {
+            for (auto& t : times)
+                std::fprintf(stderr, "[fcshard] tune op=%d M=%lld K=%lld N=%lld %s: %.4f ms\n", op, (long long)M,
+                             (long long)K, (long long)N, describe(p, t.first, 0).c_str(), t.second);
+            std::fprintf(stderr, "[fcshard] tune op=%d pick %s\n", op, pick >= 0 ? describe(p, pick, 0).c_str() : "none");
+        }
+        if (pick >= 0) {
+            std::lock_guard<std::mutex> lk(g_mu);
+            g_plans[make_key(dev, op, M, K, N, x_order, w_order, out_dtype)] = pick;
+        }
+    }
+    hipEventDestroy(ev[0]);
+    hipEventDestroy(ev[1]);
+    if (hipStreamSynchronize(s) != hipSuccess) result = FC_E_HIP;
+    return result;
+}
+
+const char* fc_status_str(fc_status status) {
+    switch (status) {
+        case FC_OK: return "FC_OK: success";
+        case FC_E_INVALID: return "FC_E_INVALID: invalid argument (NULL, dimension < 1, bad enum, misaligned or overlapping)";
+        case FC_E_UNSUPPORTED: return "FC_E_UNSUPPORTED: device is not gfx950 or plan does not apply";
+        case FC_E_HIP: return "FC_E_HIP: HIP runtime or launch error";
+        case FC_E_NOMEM: return "FC_E_NOMEM: device allocation failed";
+    }
+    return "unknown fc_status";
+}
+
+fc_status fc_release(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_plans.clear();
+    fc_status st = FC_OK;
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (g_dev[d].ws) {
+            int cur = 0;
+            if (hipGetDevice(&cur) != hipSuccess) return FC_E_HIP;
+            if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) st = FC_E_HIP;
+            hipFree(g_dev[d].ws);
+            g_dev[d].ws = nullptr;
+            g_dev[d].ws_bytes = 0;
+            hipSetDevice(cur);
+        }
+    }
+    return st;
+}
+
+}  // extern "C"

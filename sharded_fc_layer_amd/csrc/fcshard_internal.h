@@ -1,0 +1,56 @@
+// Internal interface between the C ABI (fcshard_api.hip) and the gfx950
+// kernels (gemm_bf16.hip, aux_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fcs {
+
+// One GEMM C[M x N] = A[M x K] . B[K x N] in the kernels' own terms:
+// M = output rows, N = output cols, K = reduction length. Each operand is
+// either reduction-contiguous (RC) or output-contiguous (OC):
+//   A RC: A(i, r) = A[i * lda + r]      A OC: A(i, r) = A[r * lda + i]
+//   B RC: B(r, j) = B[j * ldb + r]      B OC: B(r, j) = B[r * ldb + j]
+// C is row-major with leading dimension N (bf16 or fp32).
+struct GemmArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    void* C;
+    int64_t M, N, K;
+    int64_t lda, ldb;
+    int64_t k_split;         // reduction elements per split slice (multiple of 64)
+    int splits;              // number of reduction slices; 1 = no split
+    int64_t c_split_stride;  // elements between the slices' fp32 partial outputs
+};
+
+struct TileCfg {
+    int bm, bn;        // block tile (output rows x output cols)
+    const char* name;  // e.g. "256x256"
+};
+
+constexpr int kNumTiles = 4;
+extern const TileCfg kTiles[kNumTiles];
+constexpr int kUnalignedTile = 3;  // the one tile the unaligned kernels use
+
+// Enqueue one GEMM kernel. `aligned` selects the 16-byte vector kernels,
+// valid only when M, N, K are multiples of 8 and A, B, C are 16-byte aligned.
+hipError_t launch_gemm(int tile, bool a_oc, bool b_oc, bool out_f32, bool aligned,
+                       const GemmArgs& args, hipStream_t stream);
+
+// Name of that kernel instance, as profilers show it (for plan descriptions).
+const char* gemm_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32, bool aligned);
+
+// dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
+                                 hipStream_t stream);
+
+// out[i] = sum_{s < splits} ws[s * stride + i] (fixed order), stored bf16 or fp32.
+hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, int64_t n, int splits,
+                                int64_t stride, hipStream_t stream);
+
+// Deterministic pseudo-random bf16 fill in [-1, 1) (tuning buffers only).
+hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t stream);
+
+}  // namespace fcs

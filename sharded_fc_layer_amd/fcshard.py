@@ -1,0 +1,177 @@
+"""Thin Python binding of libfcshard.so (the C ABI declared in include/fcshard.h).
+
+Argument marshalling only: every product runs in the library's HIP kernels.
+PyTorch supplies device memory (torch.Tensor) and the current HIP stream.
+If the library is not built, every call raises: there is no fallback.
+
+Storage conventions follow the ABI: X is M x K and W is K x N as logical
+matrices, each stored row-major (ROW) or column-major (COL); a COL matrix is
+passed as the tensor of its transpose (e.g. nn.Linear.weight, N x K, is W in
+COL). dY, Y, dX and dW are row-major.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfcshard.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fcshard.h")
+
+ROW, COL = 0, 1                # fc_order
+OUT_BF16, OUT_F32 = 0, 1       # fc_out_dtype
+OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2  # fc_op
+FC_OK, FC_E_INVALID, FC_E_UNSUPPORTED, FC_E_HIP, FC_E_NOMEM = 0, 1, 2, 3, 4
+
+_lib = None
+
+
+class FcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)}")
+        self.status = status
+
+
+def header_functions() -> List[str]:
+    """Names of the functions that include/fcshard.h declares."""
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:fc_status|int|const char\*)\s+(fc_\w+)\s*\(", text, re.M)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sharded_fc_layer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci, cs = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.fc_fwd.argtypes = [vp, ci, vp, ci, vp, ci, i64, i64, i64, vp]
+        L.fc_bwd_data.argtypes = [vp, vp, ci, vp, ci, i64, i64, i64, vp]
+        L.fc_bwd_weight.argtypes = [vp, ci, vp, vp, ci, i64, i64, i64, vp]
+        L.fc_tune.argtypes = [i64, i64, i64, ci, ci, ci, ci, vp]
+        L.fc_set_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, ci]
+        L.fc_plan_describe.argtypes = [ci, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, cs]
+        L.fc_plan_count.argtypes = []
+        L.fc_status_str.argtypes = [ci]
+        L.fc_status_str.restype = ctypes.c_char_p
+        L.fc_release.argtypes = []
+        for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
+                  L.fc_plan_count, L.fc_release):
+            f.restype = ci
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fc_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != FC_OK:
+        raise FcError(status, what)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _bf16_2d(t, name: str):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D torch.bfloat16 tensor")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA/HIP tensor")
+    return t
+
+
+def _logical(t, order: int):
+    """(rows, cols) of the logical matrix whose storage is tensor t."""
+    r, c = t.shape
+    return (r, c) if order == ROW else (c, r)
+
+
+def _out(out, rows: int, cols: int, out_dtype: int, like, name: str):
+    import torch
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    if out is None:
+        return torch.empty((rows, cols), dtype=dt, device=like.device)
+    if out.dtype != dt or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {(rows, cols)}")
+    return out
+
+
+def fc_fwd(X, W, x_order: int = ROW, w_order: int = ROW, out=None, out_dtype: int = OUT_BF16, stream=None):
+    """Y = X . W on the GPU; returns Y (M x N, row-major)."""
+    _bf16_2d(X, "X"), _bf16_2d(W, "W")
+    M, K = _logical(X, x_order)
+    K2, N = _logical(W, w_order)
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: X is {M}x{K}, W is {K2}x{N}")
+    Y = _out(out, M, N, out_dtype, X, "out")
+    _check(lib().fc_fwd(X.data_ptr(), x_order, W.data_ptr(), w_order, Y.data_ptr(), out_dtype, M, K, N,
+                        _stream(stream)), "fc_fwd")
+    return Y
+
+
+def fc_bwd_data(dY, W, w_order: int = ROW, out=None, out_dtype: int = OUT_BF16, stream=None):
+    """dX = dY . W^T on the GPU; returns dX (M x K, row-major)."""
+    _bf16_2d(dY, "dY"), _bf16_2d(W, "W")
+    M, N = dY.shape
+    K, N2 = _logical(W, w_order)
+    if N2 != N:
+        raise ValueError(f"dY is {M}x{N} but W is {K}x{N2}")
+    dX = _out(out, M, K, out_dtype, dY, "out")
+    _check(lib().fc_bwd_data(dY.data_ptr(), W.data_ptr(), w_order, dX.data_ptr(), out_dtype, M, K, N,
+                             _stream(stream)), "fc_bwd_data")
+    return dX
+
+
+def fc_bwd_weight(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16, stream=None):
+    """dW = X^T . dY on the GPU; returns dW (K x N, row-major)."""
+    _bf16_2d(X, "X"), _bf16_2d(dY, "dY")
+    M, K = _logical(X, x_order)
+    M2, N = dY.shape
+    if M2 != M:
+        raise ValueError(f"X is {M}x{K} but dY is {M2}x{N}")
+    dW = _out(out, K, N, out_dtype, X, "out")
+    _check(lib().fc_bwd_weight(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
+                               _stream(stream)), "fc_bwd_weight")
+    return dW
+
+
+def fc_tune(M: int, K: int, N: int, x_order: int = ROW, w_order: int = ROW, out_dtype: int = OUT_BF16,
+            exhaustive: bool = False, stream=None) -> None:
+    """Time candidate plans of the three products at this shape and cache the fastest."""
+    _check(lib().fc_tune(M, K, N, x_order, w_order, out_dtype, 1 if exhaustive else 0, _stream(stream)),
+           "fc_tune")
+
+
+def fc_plan_count() -> int:
+    return int(lib().fc_plan_count())
+
+
+def fc_set_plan(op: int, M: int, K: int, N: int, x_order: int, w_order: int, out_dtype: int, plan_id: int) -> int:
+    """Force a plan (or -1 to clear); returns the status (no raise, for sweeps)."""
+    return int(lib().fc_set_plan(op, M, K, N, x_order, w_order, out_dtype, plan_id))
+
+
+def fc_plan_describe(op: int, M: int, K: int, N: int, x_order: int = ROW, w_order: int = ROW,
+                     out_dtype: int = OUT_BF16) -> dict:
+    """The plan a hot call would run at this key, parsed into a dict."""
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().fc_plan_describe(op, M, K, N, x_order, w_order, out_dtype, buf, 512), "fc_plan_describe")
+    text = buf.value.decode()
+    d = dict(re.findall(r"(\w+)=(gemm_bf16_kernel<[^>]*>|\S+)", text))
+    for k in ("plan", "split", "copy", "ws"):
+        d[k] = int(d[k])
+    return d
+
+
+def fc_release() -> None:
+    _check(lib().fc_release(), "fc_release")

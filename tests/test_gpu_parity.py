@@ -1,0 +1,260 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+* exact: integer-valued inputs make every fp32 partial sum exact in any
+  order, so fp32 outputs must equal the oracle bit for bit and bf16 outputs
+  must equal the oracle's nearest-even rounding of the exact value - for every
+  product, storage order, output type, odd shape and every plan the tuner can
+  pick;
+* tolerance: N(0, sigma) inputs on ragged shapes and on the five workloads at
+  full size (sampled outputs computed one by one by the oracle), with the
+  plans fc_tune picks, as the benchmark runs them: max |G - O| <= 1e-2 S
+  elementwise (S = |A|.|B|) and relative Frobenius error <= 5e-3;
+* determinism: the same plan twice gives the same bits.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from sharded_fc_layer_amd import fcshard as F
+from sharded_fc_layer_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+ROW, COL = I.ROW, I.COL
+OPS = ["fwd", "bwd_data", "bwd_weight"]
+ALL_ORDERS = [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)]
+ELEM_TOL, FRO_TOL = 1e-2, 5e-3
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def host(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class Case:
+    """Inputs of one shard on the device in given storage orders."""
+
+    def __init__(self, d, xo, wo):
+        self.d, self.xo, self.wo = d, xo, wo
+        self.M, self.K = d["X"].shape
+        self.N = d["W"].shape[1]
+        self.X = dev(I.stored(d["X"], xo))
+        self.W = dev(I.stored(d["W"], wo))
+        self.dY = dev(d["dY"])
+
+    def gpu(self, op, out_dtype):
+        if op == "fwd":
+            return F.fc_fwd(self.X, self.W, self.xo, self.wo, out_dtype=out_dtype)
+        if op == "bwd_data":
+            return F.fc_bwd_data(self.dY, self.W, self.wo, out_dtype=out_dtype)
+        return F.fc_bwd_weight(self.X, self.dY, self.xo, out_dtype=out_dtype)
+
+    def oracle(self, op, rows=None, cols=None):
+        d, M, K, N = self.d, self.M, self.K, self.N
+        if op == "fwd":
+            return oracle.fc_fwd(I.stored(d["X"], self.xo), self.xo, I.stored(d["W"], self.wo), self.wo, M, K, N,
+                                 rows, cols)
+        if op == "bwd_data":
+            return oracle.fc_bwd_data(d["dY"], I.stored(d["W"], self.wo), self.wo, M, K, N, rows, cols)
+        return oracle.fc_bwd_weight(I.stored(d["X"], self.xo), self.xo, d["dY"], M, K, N, rows, cols)
+
+
+def op_code(op):
+    return {"fwd": F.OP_FWD, "bwd_data": F.OP_BWD_DATA, "bwd_weight": F.OP_BWD_WEIGHT}[op]
+
+
+def assert_exact(G: np.ndarray, O: np.ndarray, out_dtype: int, what: str):
+    if out_dtype == F.OUT_F32:
+        want = O.astype(np.float32)
+        assert np.array_equal(want.astype(np.float64), O), "oracle value not exact in fp32"
+        bad = np.argwhere(G.view(np.uint32) != want.view(np.uint32))
+    else:
+        want = oracle.round_bf16(O)
+        bad = np.argwhere(G != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+
+def assert_close(G: np.ndarray, O: np.ndarray, S: np.ndarray, out_dtype: int, what: str):
+    Gv = I.bf16_bits_to_f32(G) if out_dtype == F.OUT_BF16 else G
+    r = oracle.compare(Gv, O, S, ELEM_TOL, FRO_TOL)
+    log(f"  {what}: max_err_ratio={r['max_err_ratio']:.3g} rel_fro={r['rel_fro']:.3g}")
+    assert r["pass"], f"{what}: {r}"
+
+
+@pytest.fixture(autouse=True)
+def _clean_plans():
+    yield
+    torch.cuda.synchronize()
+    F.fc_release()
+
+
+# ------------------------------------------------------------- exact parity
+
+EXACT_SHAPES = [(1, 1, 1), (7, 33, 17), (33, 7, 65), (130, 257, 129), (8, 16, 24), (264, 520, 136),
+                (256, 512, 256), (520, 136, 1032)]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_exact_integer_default_plans(shape):
+    M, K, N = shape
+    d = I.make_integer_inputs(M, K, N, seed=1)
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        for op in OPS:
+            O, _ = c.oracle(op)
+            for dt in (F.OUT_BF16, F.OUT_F32):
+                what = f"{op} {shape} orders={xo}{wo} dtype={dt}"
+                log(what)
+                G = host(c.gpu(op, dt))
+                torch.cuda.synchronize()
+                assert_exact(G, O, dt, what)
+
+
+def test_exact_power_of_two_scaled_inputs():
+    # integers times powers of two: still exact; exercises exponent handling
+    M, K, N = 136, 264, 72
+    d = I.make_integer_inputs(M, K, N, seed=2, pow2=(-6, 3, -2))
+    c = Case(d, ROW, ROW)
+    for op in OPS:
+        O, _ = c.oracle(op)
+        for dt in (F.OUT_BF16, F.OUT_F32):
+            assert_exact(host(c.gpu(op, dt)), O, dt, f"{op} pow2 dtype={dt}")
+
+
+@pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_exact_integer_every_plan(shape):
+    M, K, N = shape
+    d = I.make_integer_inputs(M, K, N, seed=3)
+    n_plans = F.fc_plan_count()
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        for op in OPS:
+            O, _ = c.oracle(op)
+            for dt in (F.OUT_BF16, F.OUT_F32):
+                ran = 0
+                for pid in range(n_plans):
+                    st = F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, pid)
+                    if st == F.FC_E_UNSUPPORTED:
+                        continue
+                    assert st == F.FC_OK, F.status_str(st)
+                    desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, dt)
+                    assert desc["plan"] == pid
+                    what = f"{op} {shape} orders={xo}{wo} dtype={dt} plan={pid} {desc['kernel']}"
+                    log(what)
+                    G = host(c.gpu(op, dt))
+                    torch.cuda.synchronize()
+                    assert_exact(G, O, dt, what)
+                    ran += 1
+                assert ran >= 1
+                F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, -1)
+
+
+# --------------------------------------------------------- tolerance parity
+
+@pytest.mark.parametrize("dt", [F.OUT_BF16, F.OUT_F32])
+def test_workload1_full(dt):
+    d = I.make_inputs(1, 1)
+    c = Case(d, ROW, ROW)
+    for op in OPS:
+        O, S = c.oracle(op)
+        assert_close(host(c.gpu(op, dt)), O, S, dt, f"workload1 {op} dtype={dt}")
+
+
+@pytest.mark.parametrize("shape", [(777, 1000, 555), (1000, 264, 1304), (513, 2056, 257), (64, 4104, 72)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ragged_tolerance_all_orders(shape):
+    M, K, N = shape
+    d = I.make_random_inputs(M, K, N, seed=4)
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        F.fc_tune(M, K, N, xo, wo, F.OUT_BF16)
+        for op in OPS:
+            O, S = c.oracle(op)
+            desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, F.OUT_BF16)
+            assert_close(host(c.gpu(op, F.OUT_BF16)), O, S, F.OUT_BF16,
+                         f"{op} {shape} orders={xo}{wo} {desc['kernel']} split={desc['split']} copy={desc['copy']}")
+
+
+def _sample(n: int, k: int, rng) -> np.ndarray:
+    pick = set(rng.choice(n, min(k, n), replace=False).tolist())
+    pick.update({0, n - 1, max(0, n - 2)})
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+FULL = [(2, 1, [(ROW, ROW)]), (2, 2, [(ROW, ROW)]), (2, 3, [(ROW, ROW)]), (2, 4, [(ROW, ROW)]),
+        (3, 1, [(ROW, ROW)]), (4, 1, I.ORDER_PAIRS),
+        (5, 1, [(ROW, ROW)]), (5, 2, [(ROW, ROW)]), (5, 3, [(ROW, ROW)]), (5, 4, [(ROW, ROW)]),
+        (5, 5, [(ROW, ROW)])]
+
+
+@pytest.mark.parametrize("workload,gemm,orders", FULL,
+                         ids=[f"w{w}g{g}" for w, g, _ in FULL])
+def test_full_size_sampled(workload, gemm, orders):
+    """Full-size shard, tuned plans as in the benchmark, sampled outputs."""
+    g = I.WORKLOADS[workload][gemm - 1]
+    log(f"workload {workload} gemm {gemm} {g}")
+    d = I.make_inputs(workload, gemm)
+    rng = np.random.default_rng([workload, gemm])
+    for xo, wo in orders:
+        c = Case(d, xo, wo)
+        F.fc_tune(g.M, g.K, g.N, xo, wo, F.OUT_BF16)
+        for op in OPS:
+            desc = F.fc_plan_describe(op_code(op), g.M, g.K, g.N, xo, wo, F.OUT_BF16)
+            what = f"w{workload}g{gemm} {op} orders={xo}{wo} {desc['kernel']} split={desc['split']} copy={desc['copy']}"
+            log(what)
+            Gt = c.gpu(op, F.OUT_BF16)
+            G2 = c.gpu(op, F.OUT_BF16)
+            torch.cuda.synchronize()
+            assert torch.equal(Gt.view(torch.int16), G2.view(torch.int16)), "not deterministic"
+            n_r, n_c = Gt.shape
+            rows, cols = _sample(n_r, 24, rng), _sample(n_c, 160, rng)
+            O, S = c.oracle(op, rows, cols)
+            G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+            assert_close(G, O, S, F.OUT_BF16, what)
+            del Gt, G2
+        del c
+        torch.cuda.empty_cache()
+
+
+# -------------------------------------------------------------- ABI on GPU
+
+def test_overlapping_output_rejected_on_device():
+    X = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    st = F.lib().fc_fwd(X.data_ptr(), 0, W.data_ptr(), 0, X.data_ptr(), 0, 64, 64, 64, None)
+    assert st == F.FC_E_INVALID
+
+
+def test_runs_on_a_side_stream_and_tuned_equals_cold_plan_bits():
+    M, K, N = 1024, 768, 1280
+    d = I.make_random_inputs(M, K, N, seed=5)
+    c = Case(d, ROW, ROW)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        cold = c.gpu("fwd", F.OUT_BF16)
+    s.synchronize()
+    desc = F.fc_plan_describe(F.OP_FWD, M, K, N)
+    F.fc_set_plan(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16, desc["plan"])
+    warm = c.gpu("fwd", F.OUT_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(cold.view(torch.int16), warm.view(torch.int16))
+    O, S = c.oracle("fwd")
+    assert_close(host(cold), O, S, F.OUT_BF16, "side stream fwd")
