@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's FC-layer shard GEMMs (forward + both backward
+products) on an MI355X, through the library's C ABI.
+
+A step is one pass of the hot path over one batch of synthetic inputs: for
+every FC layer of the workload, forward Y = X.W, backward-data dX = dY.W^T
+and backward-weight dW = X^T.dY, issued back to back on one HIP stream
+(bf16 in, fp32 accumulate, bf16 out), with the plans fc_tune picked (tuning
+runs before the timed region). Inputs are resident in HBM before timing.
+
+Default workload: the GPT-style block with hidden 2048 and 8192 tokens
+(QKV 2048->6144, attention-out 2048->2048, MLP up 2048->8192, MLP down
+8192->2048), i.e. 12 GEMMs per step.
+
+Prints ONE JSON line. `value` is TFLOP/s (2 M K N per GEMM, summed over the
+step, divided by the mean step time). `roofline` reports the dominant kernel
+(largest summed time) against the dense bf16 MFMA peak, from HIP events
+recorded on the launch stream around each of its launches. `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_NAMES = {
+    1: "single_fc_256x512x2048",
+    2: "gpt_block_h2048_t8192",
+    3: "mlp_up_shard_h12288_2x2x2",
+    4: "skinny_shard_h16384_gx8_gy8",
+    5: "llm405b_like_layer_2x4x2_plus_vocab",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--no-extra", action="store_true", help="skip the large-shard context workloads")
+    p.add_argument("--no-tune", action="store_true", help="use the default plans")
+    p.add_argument("--plans", default=None,
+                   help="plan file: loaded if it exists (no tuning in this run), else written after tuning")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    return p.parse_args()
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+class Layer:
+    """Device buffers of one FC shard and the three calls of a step."""
+
+    def __init__(self, g, X, W, dY, torch, F):
+        self.g, self.F = g, F
+        self.X, self.W, self.dY = X, W, dY
+        self.Y = torch.empty((g.M, g.N), dtype=torch.bfloat16, device="cuda")
+        self.dX = torch.empty((g.M, g.K), dtype=torch.bfloat16, device="cuda")
+        self.dW = torch.empty((g.K, g.N), dtype=torch.bfloat16, device="cuda")
+
+    def calls(self):
+        F = self.F
+        return [
+            ("fwd", F.OP_FWD, lambda: F.fc_fwd(self.X, self.W, out=self.Y)),
+            ("bwd_data", F.OP_BWD_DATA, lambda: F.fc_bwd_data(self.dY, self.W, out=self.dX)),
+            ("bwd_weight", F.OP_BWD_WEIGHT, lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW)),
+        ]
+
+
+def make_layers(workload, torch, F, I, host_inputs):
+    import numpy as np
+    layers = []
+    for gi, g in enumerate(I.WORKLOADS[workload], start=1):
+        if host_inputs:
+            d = I.make_inputs(workload, gi)
+            dev = lambda b: torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16)  # noqa: E731
+            layers.append(Layer(g, dev(d["X"]), dev(d["W"]), dev(d["dY"]), torch, F))
+            del d
+        else:
+            gen = torch.Generator(device="cuda").manual_seed(1000 * workload + gi)
+            rn = lambda r, c, s: (torch.randn((r, c), device="cuda", generator=gen) * s).to(torch.bfloat16)  # noqa
+            layers.append(Layer(g, rn(g.M, g.K, g.sx), rn(g.K, g.N, g.sw), rn(g.M, g.N, g.sdy), torch, F))
+    return layers
+
+
+def step_calls(layers):
+    """Training-step order: forwards layer by layer, then backwards in reverse."""
+    fw = [(L, c) for L in layers for c in L.calls()[:1]]
+    bw = [(L, c) for L in reversed(layers) for c in L.calls()[1:]]
+    return fw + bw
+
+
+def step_flops(layers):
+    return sum(3 * L.g.flops for L in layers)
+
+
+def run_timed(layers, steps, warmup, torch):
+    calls = step_calls(layers)
+    for _ in range(warmup):
+        for _, (_, _, fn) in calls:
+            fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(steps):
+        for _, (_, _, fn) in calls:
+            fn()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[steps])
+    return total_ms / steps, per_step, wall
+
+
+def run_per_launch(layers, steps, torch, F):
+    """Per-call HIP events on the launch stream: {kernel: [durations ms]}."""
+    calls = step_calls(layers)
+    stream = torch.cuda.current_stream()
+    recs = []
+    for _ in range(steps):
+        for L, (opname, op, fn) in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            recs.append((L, op, a, b))
+    torch.cuda.synchronize()
+    out = {}
+    for L, op, a, b in recs:
+        g = L.g
+        desc = F.fc_plan_describe(op, g.M, g.K, g.N)
+        key = desc["kernel"]
+        single = desc["split"] == 1 and desc["copy"] == 0
+        e = out.setdefault(key, {"ms": [], "flops": [], "single_launch": True})
+        e["ms"].append(a.elapsed_time(b))
+        e["flops"].append(g.flops)
+        e["single_launch"] = e["single_launch"] and single
+    return out
+
+
+def plans_of(layers, F):
+    res = []
+    for L in layers:
+        g = L.g
+        for opname, op, _ in L.calls():
+            d = F.fc_plan_describe(op, g.M, g.K, g.N)
+            res.append({"gemm": g.name, "op": opname, "M": g.M, "K": g.K, "N": g.N, "kernel": d["kernel"],
+                        "split": d["split"], "copy": d["copy"]})
+    return res
+
+
+def cpu_baseline(workload, target_s, I):
+    """The oracle as it stands, on sampled output rows of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        cores = ctypes.CDLL("libgomp.so.1").omp_get_max_threads()
+    except OSError:
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    gemms = I.WORKLOADS[workload]
+    inputs = [I.make_inputs(workload, gi) for gi in range(1, len(gemms) + 1)]
+
+    def one(gi, op, rows):
+        g, d = gemms[gi], inputs[gi]
+        if op == "fwd":
+            oracle.fc_fwd(d["X"], 0, d["W"], 0, g.M, g.K, g.N, rows=rows)
+            return 2 * len(rows) * g.K * g.N
+        if op == "bwd_data":
+            oracle.fc_bwd_data(d["dY"], d["W"], 0, g.M, g.K, g.N, rows=rows)
+            return 2 * len(rows) * g.N * g.K
+        oracle.fc_bwd_weight(d["X"], 0, d["dY"], g.M, g.K, g.N, rows=rows)
+        return 2 * len(rows) * g.M * g.N
+
+    ops = ["fwd", "bwd_data", "bwd_weight"]
+
+    def one_pass(rows_each):
+        t = time.perf_counter()
+        fl = 0
+        for gi in range(len(gemms)):
+            for op in ops:
+                n_out_rows = gemms[gi].K if op == "bwd_weight" else gemms[gi].M
+                rows = np.linspace(0, n_out_rows - 1, min(rows_each, n_out_rows)).astype(np.int64)
+                fl += one(gi, op, rows)
+        return fl, time.perf_counter() - t
+
+    # double the sample until one pass takes at least half the target time
+    rows_each = 8
+    while True:
+        flops, dt = one_pass(rows_each)
+        if dt >= 0.5 * target_s or rows_each >= 8192:
+            break
+        rows_each *= 2
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_each} full output rows of each of the {3 * len(gemms)} GEMMs of the workload "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s; fp64 plain loops, OpenMP)",
+            "seconds": dt, "cpu": cpu}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from sharded_fc_layer_amd import fcshard as F
+    from sharded_fc_layer_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    F.lib()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')}; workload {args.workload}")
+    t = time.perf_counter()
+    layers = make_layers(args.workload, torch, F, I, host_inputs=True)
+    log(f"inputs resident ({time.perf_counter() - t:.1f} s)")
+    tune_s = 0.0
+    if args.plans and os.path.exists(args.plans):
+        F.fc_plans_load(args.plans)
+        log(f"loaded plans from {args.plans}")
+    elif not args.no_tune:
+        t = time.perf_counter()
+        for L in layers:
+            F.fc_tune(L.g.M, L.g.K, L.g.N)
+        torch.cuda.synchronize()
+        tune_s = time.perf_counter() - t
+        log(f"tuned {len(layers)} shapes in {tune_s:.1f} s")
+        if args.plans:
+            F.fc_plans_save(args.plans)
+
+    ms, per_step, wall = run_timed(layers, args.steps, args.warmup, torch)
+    flops = step_flops(layers)
+    value = flops / (ms / 1e3) / 1e12
+    log(f"{ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    kern = run_per_launch(layers, args.steps, torch, F)
+    dom = max(kern.items(), key=lambda kv: sum(kv[1]["ms"]))
+    dname, drec = dom
+    d_avg_ms = float(np.mean(drec["ms"]))
+    d_avg_flops = float(np.mean(drec["flops"]))
+    achieved = d_avg_flops / (d_avg_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dname,
+                "launches": len(drec["ms"]), "avg_launch_us": round(d_avg_ms * 1e3, 2),
+                "avg_gflop_per_launch": round(d_avg_flops / 1e9, 3),
+                "single_launch_plans": drec["single_launch"]}
+    per_kernel = {k: {"launches": len(v["ms"]), "avg_us": round(float(np.mean(v["ms"])) * 1e3, 2),
+                      "tflops": round(float(np.sum(v["flops"]) / (np.sum(v["ms"]) / 1e3) / 1e12), 1)}
+                  for k, v in kern.items()}
+
+    last8 = per_step[-8:] if len(per_step) >= 10 else per_step
+    result = {
+        "metric": "bf16 TFLOP/s of FC fwd+bwd shard GEMMs on 1 MI355X; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": I.WORKLOADS[args.workload][0].M,
+                   "gemms": [[g.name, g.M, g.K, g.N] for g in I.WORKLOADS[args.workload]],
+                   "products_per_gemm": ["fwd", "bwd_data", "bwd_weight"], "orders": "X row, W row",
+                   "out_dtype": "bf16", "step_gflop": round(flops / 1e9, 2)},
+        "pct_of_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "step_ms_stats": {"mean_last8": round(float(np.mean(last8)), 4), "median": round(float(np.median(per_step)), 4),
+                          "min": round(float(np.min(per_step)), 4), "max": round(float(np.max(per_step)), 4)},
+        "roofline": roofline,
+        "per_kernel": per_kernel,
+        "plans": plans_of(layers, F),
+        "tune_s": round(tune_s, 2),
+        "device": props.name,
+    }
+
+    if not args.no_extra:
+        extra = {}
+        del layers
+        torch.cuda.empty_cache()
+        for w in (3, 5):
+            Ls = make_layers(w, torch, F, I, host_inputs=False)
+            if not args.no_tune:
+                for L in Ls:
+                    F.fc_tune(L.g.M, L.g.K, L.g.N)
+            wms, wsteps, _ = run_timed(Ls, 10, 3, torch)
+            wf = step_flops(Ls)
+            extra[WORKLOAD_NAMES[w]] = {"tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
+                                        "pct_of_mfma_peak": round(100 * wf / (wms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+                                        "gemms_per_step": 3 * len(Ls)}
+            log(f"workload {w}: {extra[WORKLOAD_NAMES[w]]}")
+            del Ls
+            torch.cuda.empty_cache()
+        result["large_shard_context"] = extra
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, I)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

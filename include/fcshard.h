@@ -122,6 +122,21 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
 fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order,
                            fc_order w_order, fc_out_dtype out_dtype, char* buf, size_t len);
 
+/*
+ * Writes every cached plan of the current device to a text file, one line
+ * "<arch> <op> <M> <K> <N> <x_order> <w_order> <out_dtype> <plan_id>".
+ * FC_E_INVALID if path is NULL or the file cannot be written.
+ */
+fc_status fc_plans_save(const char* path);
+
+/*
+ * Reads such a file and caches, for the current device, every line whose
+ * arch matches it (growing the workspace as the plans need). Lines for other
+ * archs are skipped. FC_E_INVALID if the file cannot be read or a line is
+ * malformed (entries before it stay loaded).
+ */
+fc_status fc_plans_load(const char* path);
+
 /* static text for a status; never NULL */
 const char* fc_status_str(fc_status status);
 

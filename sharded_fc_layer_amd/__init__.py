@@ -21,6 +21,8 @@ from .fcshard import (  # noqa: F401
     fc_fwd,
     fc_plan_count,
     fc_plan_describe,
+    fc_plans_load,
+    fc_plans_save,
     fc_release,
     fc_set_plan,
     fc_tune,

@@ -138,6 +138,7 @@ struct Key {
 
 struct DevState {
     int checked = 0;  // 0 unknown, 1 gfx950, -1 other
+    char arch[64] = {0};
     void* ws = nullptr;
     int64_t ws_bytes = 0;
 };
@@ -165,6 +166,9 @@ fc_status check_device(int* dev_out) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FC_E_HIP;
         d.checked = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        std::snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+        for (char* c = d.arch; *c; ++c)
+            if (*c == ' ' || *c == '\n') *c = '_';
     }
     return d.checked == 1 ? FC_OK : FC_E_UNSUPPORTED;
 }
@@ -560,6 +564,55 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
     hipEventDestroy(ev[0]);
     hipEventDestroy(ev[1]);
     if (hipStreamSynchronize(s) != hipSuccess) result = FC_E_HIP;
+    return result;
+}
+
+fc_status fc_plans_save(const char* path) {
+    if (!path) return FC_E_INVALID;
+    std::lock_guard<std::mutex> lk(g_mu);
+    int dev;
+    fc_status st = check_device(&dev);
+    if (st != FC_OK) return st;
+    FILE* f = std::fopen(path, "w");
+    if (!f) return FC_E_INVALID;
+    for (const auto& kv : g_plans) {
+        const Key& k = kv.first;
+        if (k.dev != dev) continue;
+        std::fprintf(f, "%s %d %lld %lld %lld %d %d %d %d\n", g_dev[dev].arch, k.op, (long long)k.M, (long long)k.K,
+                     (long long)k.N, k.xo, k.wo, k.f32, kv.second);
+    }
+    return std::fclose(f) == 0 ? FC_OK : FC_E_INVALID;
+}
+
+fc_status fc_plans_load(const char* path) {
+    if (!path) return FC_E_INVALID;
+    int dev;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        fc_status st = check_device(&dev);
+        if (st != FC_OK) return st;
+    }
+    FILE* f = std::fopen(path, "r");
+    if (!f) return FC_E_INVALID;
+    char line[512];
+    fc_status result = FC_OK;
+    while (std::fgets(line, sizeof line, f)) {
+        char arch[64];
+        int op, xo, wo, f32, id;
+        long long M, K, N;
+        if (line[0] == '\n' || line[0] == '#') continue;
+        if (std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d", arch, &op, &M, &K, &N, &xo, &wo, &f32, &id) != 9) {
+            result = FC_E_INVALID;
+            break;
+        }
+        if (std::strcmp(arch, g_dev[dev].arch) != 0) continue;
+        fc_status st = fc_set_plan((fc_op)op, M, K, N, (fc_order)xo, (fc_order)wo, (fc_out_dtype)f32, id);
+        if (st != FC_OK) {
+            result = st;
+            break;
+        }
+    }
+    std::fclose(f);
     return result;
 }
 

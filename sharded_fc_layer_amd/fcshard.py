@@ -58,8 +58,10 @@ def lib() -> ctypes.CDLL:
         L.fc_status_str.argtypes = [ci]
         L.fc_status_str.restype = ctypes.c_char_p
         L.fc_release.argtypes = []
+        L.fc_plans_save.argtypes = [ctypes.c_char_p]
+        L.fc_plans_load.argtypes = [ctypes.c_char_p]
         for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
-                  L.fc_plan_count, L.fc_release):
+                  L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load):
             f.restype = ci
         _lib = L
     return _lib
@@ -171,6 +173,16 @@ def fc_plan_describe(op: int, M: int, K: int, N: int, x_order: int = ROW, w_orde
     for k in ("plan", "split", "copy", "ws"):
         d[k] = int(d[k])
     return d
+
+
+def fc_plans_save(path: str) -> None:
+    """Write the current device's cached plans to a text file."""
+    _check(lib().fc_plans_save(os.fsencode(path)), "fc_plans_save")
+
+
+def fc_plans_load(path: str) -> None:
+    """Load plans saved by fc_plans_save (entries for this device's arch)."""
+    _check(lib().fc_plans_load(os.fsencode(path)), "fc_plans_load")
 
 
 def fc_release() -> None:

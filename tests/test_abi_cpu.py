@@ -25,7 +25,7 @@ def L():
 def test_header_declares_the_boundary():
     names = F.header_functions()
     for n in ("fc_fwd", "fc_bwd_data", "fc_bwd_weight", "fc_tune", "fc_status_str", "fc_release",
-              "fc_set_plan", "fc_plan_describe", "fc_plan_count"):
+              "fc_set_plan", "fc_plan_describe", "fc_plan_count", "fc_plans_save", "fc_plans_load"):
         assert n in names
 
 
