@@ -35,22 +35,31 @@ namespace {
 
 constexpr int kSplits[] = {1, 2, 4};
 constexpr int kNumSplits = 3;
-constexpr int kNumCopy = 4;  // bit 0: copy A to RC, bit 1: copy B to RC
-constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy;
+constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
+// 0: pipelined, 1: simple, 2: 8-wave ping-pong with 48-value stages, 3: with 32-value stages
+constexpr int kNumFamilies = 4;
+constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
+constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
 constexpr int kMaxDevices = 64;
 
 struct Plan {
     int tile;
-    int split;  // number of reduction slices requested
-    int copy;   // bit mask
+    int split;   // number of reduction slices requested
+    int copy;    // bit mask
+    int family;  // 0 pipelined, 1 simple, 2/3 ping-pong (48/32-value stages)
 };
 
 Plan decode_plan(int id) {
     Plan p;
     p.tile = id % kNumTiles;
     p.split = kSplits[(id / kNumTiles) % kNumSplits];
-    p.copy = id / (kNumTiles * kNumSplits);
+    p.copy = (id / (kNumTiles * kNumSplits)) % kNumCopy;
+    p.family = id / (kNumTiles * kNumSplits * kNumCopy);
     return p;
+}
+
+int encode_plan(int tile, int split_idx, int copy, int family) {
+    return tile + kNumTiles * (split_idx + kNumSplits * (copy + kNumCopy * family));
 }
 
 // One GEMM in kernel terms, resolved from an ABI call.
@@ -115,7 +124,15 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     (uintptr_t)p.C % 16 == 0 &&
                                     ((pl.copy & 1) || (uintptr_t)p.A % 16 == 0) &&
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
-    if (!aligned_after_copy && pl.tile != kUnalignedTile) return false;
+    if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
+    if (pl.family >= 2 && pl.tile != 0) return false;
+    if (pl.family != 1) {
+        const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * p.K * 2);
+        const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * p.K * 2);
+        if (a_bytes >= kPipeMaxBytes || b_bytes >= kPipeMaxBytes || p.M * p.K * 2 >= kPipeMaxBytes ||
+            p.N * p.K * 2 >= kPipeMaxBytes)
+            return false;
+    }
     if (pl.split > 1) {
         int64_t ks;
         int slices;
@@ -176,13 +193,23 @@ fc_status check_device(int* dev_out) {
 // default plan: no workspace, no split; the largest tile that still gives
 // every CU work
 int default_plan(const Problem& p) {
-    if (!problem_aligned(p)) return kUnalignedTile;
-    int cus = 256;
+    const int unaligned = encode_plan(kUnalignedTile, 0, 0, 1);
+    if (!problem_aligned(p)) return unaligned;
+    const int cus = 256;
+    int tile = kUnalignedTile;  // 128x128
     for (int t = 0; t < kNumTiles; ++t) {
         const int64_t tiles = ((p.M + kTiles[t].bm - 1) / kTiles[t].bm) * ((p.N + kTiles[t].bn - 1) / kTiles[t].bn);
-        if (tiles >= cus) return t;
+        if (tiles >= cus) {
+            tile = t;
+            break;
+        }
     }
-    return kUnalignedTile;  // 128x128 (also valid aligned)
+    // 256x256 tiles filling the chip: the 8-wave ping-pong kernel; otherwise
+    // the 4-wave pipelined kernel with the largest tile that still does
+    const int pp = encode_plan(0, 0, 0, 3);
+    if (tile == 0 && plan_applies(p, decode_plan(pp))) return pp;
+    const int pipe = encode_plan(tile, 0, 0, 0);
+    return plan_applies(p, decode_plan(pipe)) ? pipe : encode_plan(tile, 0, 0, 1);
 }
 
 // ------------------------------------------------------------- execution
@@ -226,11 +253,16 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
         float* part = reinterpret_cast<float*>(base + w.p_off);
         g.C = part;
         g.c_split_stride = p.M * p.N;
-        if ((e = launch_gemm(pl.tile, p.a_oc, p.b_oc, true, true && aligned, g, s)) != hipSuccess) return e;
+        e = pl.family == 0   ? launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, true, g, s)
+            : pl.family >= 2 ? launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, true, g, s)
+                             : launch_gemm(pl.tile, p.a_oc, p.b_oc, true, aligned, g, s);
+        if (e != hipSuccess) return e;
         return launch_splitk_reduce(part, p.C, p.out_f32, p.M * p.N, slices, p.M * p.N, s);
     }
     g.C = p.C;
     g.c_split_stride = 0;
+    if (pl.family == 0) return launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, p.out_f32, g, s);
+    if (pl.family >= 2) return launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, p.out_f32, g, s);
     return launch_gemm(pl.tile, p.a_oc, p.b_oc, p.out_f32, aligned, g, s);
 }
 
@@ -344,8 +376,11 @@ std::string describe(const Problem& p, int id, int64_t ws_have) {
     const bool aligned = q.M % 8 == 0 && q.N % 8 == 0 && q.K % 8 == 0 &&
                          (uintptr_t)p.C % 16 == 0 && (q.A == nullptr || (uintptr_t)q.A % 16 == 0) &&
                          (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
-    const char* kname = gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc,
-                                         slices > 1 ? true : p.out_f32, aligned);
+    const bool f32 = slices > 1 ? true : p.out_f32;
+    const char* kname = pl.family == 0   ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
+                        : pl.family >= 2 ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
+                                         : gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc, f32,
+                                                            aligned);
     char buf[512];
     std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname,
                   kTiles[aligned ? pl.tile : kUnalignedTile].name, slices, pl.copy,
@@ -513,6 +548,8 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
             const Plan pl = decode_plan(id);
             if (!plan_applies(p, pl)) continue;
             if (!exhaustive && pl.split > 1 && pl.copy != 0) continue;
+            // the simple kernels only win on unaligned shapes
+            if (!exhaustive && pl.family == 1 && problem_aligned(p)) continue;
             cand.push_back(id);
             need = std::max(need, ws_layout(p, pl).total);
         }

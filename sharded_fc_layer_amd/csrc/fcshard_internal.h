@@ -42,6 +42,19 @@ hipError_t launch_gemm(int tile, bool a_oc, bool b_oc, bool out_f32, bool aligne
 // Name of that kernel instance, as profilers show it (for plan descriptions).
 const char* gemm_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32, bool aligned);
 
+// Enqueue one pipelined GEMM kernel (gemm_pipe.hip). Valid only when M, N,
+// K are multiples of 8, A, B, C are 16-byte aligned and A and B each span
+// less than 2 GiB.
+hipError_t launch_gemm_pipe(int tile, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+                            hipStream_t stream);
+const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32);
+
+// Enqueue the 8-wave ping-pong GEMM (256 x 256 tile; same requirements as
+// launch_gemm_pipe). depth 0: 48-value reduction stages, 1: 32-value stages.
+hipError_t launch_gemm_pingpong(int depth, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+                                hipStream_t stream);
+const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32);
+
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                  hipStream_t stream);

@@ -1,0 +1,576 @@
+// Pipelined bf16 GEMM for gfx950 (MI355X): the main kernels of the three
+// local products of one GPU's FC-layer shard under the 3D parallel matrix
+// multiply (sciencestack.ai/paper/2502.08145, Figure 1), bf16 in with fp32
+// accumulation (mlsanity.com/paper/2502.08145, Abstract: bf16 training).
+//
+// Requirements (checked by the caller): M, N, K multiples of 8, 16-byte
+// aligned operands and output, every operand smaller than 2 GiB.
+//
+// Structure (256 threads = 4 wave64s in a 2 x 2 grid, block tile BM x BN):
+//  * Reduction stages of 32 values; a ring of 4 LDS stages. Global data goes
+//    straight into LDS with buffer_load ... lds (16 bytes per lane), no
+//    register staging. Stage t + 4 is requested as soon as every wave has
+//    finished reading stage t, i.e. three stages of MFMA work ahead.
+//  * Out-of-range chunks (tile tails in M, N and the reduction) are given an
+//    offset past the buffer's size, so the hardware fills them with zeros.
+//  * Reduction-contiguous operands: LDS row = one tile row, 32 values (64 B),
+//    16-byte chunk index XOR-swizzled with (row >> 2) & 3; MFMA operands are
+//    single ds_read_b128.
+//  * Output-contiguous operands are stored untransposed (LDS row = one
+//    reduction index, chunk index XOR-swizzled with (k & 3) << 2) and read
+//    with ds_read_b64_tr_b16: within each 16-lane group, lane j addresses
+//    reduction row k0 + j / 4 at columns base + 4 (j % 4), and lane i
+//    receives the four reduction values k0 .. k0+3 of column base + i. Two
+//    such reads give one 8-value MFMA operand.
+//  * Per stage, each wave runs two 16-deep steps of v_mfma_f32_32x32x16_bf16
+//    over its (BM/2) x (BN/2) sub-tile. The operands of the first step of the
+//    next stage are read right after the stage barrier, which itself sits
+//    between the two MFMA steps of the current stage, so MFMA issue
+//    continues across the barrier.
+//  * MFMAs take the B fragment as source A, so each lane's accumulators hold
+//    4 consecutive output columns of one output row (vector stores).
+//  * Blocks are remapped so that each XCD works through one contiguous range
+//    of tiles, in groups of 8 tile-rows (L2 sharing within an XCD).
+//  * Reduction slices (split-K) write fp32 partials to separate planes.
+#include "fcshard_internal.h"
+
+namespace fcs {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+constexpr int kBK = 32;        // reduction values per stage
+constexpr int kStages = 4;     // LDS ring depth
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+constexpr uint32_t kOOB = 0x80000000u;       // offset past any operand (< 2 GiB)
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
+
+__device__ __forceinline__ uint32_t rc_slot(int i, int c) { return i * 64 + ((c ^ ((i >> 2) & 3)) << 4); }
+
+template <int R>
+__device__ __forceinline__ uint32_t oc_slot(int k, int c) {
+    return k * (R * 2) + ((c ^ ((k & 3) << 2)) << 4);
+}
+
+// s_waitcnt with vmcnt = vm, lgkmcnt = lgkm (expcnt not waited)
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
+}
+
+// One operand tile of R rows (output index) x 32 reduction values per stage.
+template <int R, bool OC>
+struct Dma {
+    static constexpr int kInstr = R / 64;  // 1 KB instructions per wave per stage
+    uint32_t base[kInstr];                 // byte offset at reduction 0, or kOOB
+    int kk[kInstr];                        // reduction offset of the chunk within a stage
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int64_t row0, int64_t rows) {
+#pragma unroll
+        for (int j = 0; j < kInstr; ++j) {
+            if (!OC) {
+                const int i = (wave * kInstr + j) * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ ((lane >> 4) & 3);
+                kk[j] = 8 * c;
+                base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
+            } else {
+                constexpr int CPR = R / 8;     // 16-byte chunks per reduction row
+                constexpr int RPI = 64 / CPR;  // reduction rows per instruction
+                const int k = (wave * kInstr + j) * RPI + lane / CPR;
+                const int c = (lane % CPR) ^ ((k & 3) << 2);
+                kk[j] = k;
+                base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
+            }
+        }
+    }
+
+    // issue instructions j in [lo, hi) of this wave's share of one stage
+    template <int LO, int HI>
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* region, int64_t k0, int64_t kend,
+                                          int64_t ld, int wave) const {
+        const uint32_t step = OC ? (uint32_t)(k0 * ld * 2) : (uint32_t)(k0 * 2);
+#pragma unroll
+        for (int j = (LO > 0 ? LO : 0); j < (HI < kInstr ? HI : kInstr); ++j) {
+            const uint32_t off = (base[j] == kOOB || k0 + kk[j] >= kend) ? kOOB : base[j] + step;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wave * kInstr + j) * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
+    }
+};
+
+// MFMA operand of one 32-row block (rows r0 .. r0+31), reduction step ks (16 values)
+template <int R, bool OC>
+__device__ __forceinline__ bf16x8 fragment(const char* region, int r0, int ks, int lane) {
+    if (!OC) {
+        const int i = r0 + (lane & 31);
+        const int c = ks * 2 + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
+    } else {
+        const int g = lane >> 4, j = lane & 15;
+        const int col = r0 + 16 * (g & 1) + 4 * (j & 3);
+        const int k = ks * 16 + 8 * (g >> 1) + (j >> 2);
+        const int c = col >> 3, half = (col & 7) << 1;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(region + oc_slot<R>(k, c) + half));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(region + oc_slot<R>(k + 4, c) + half));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+template <int BM, int BN, bool A_OC, bool B_OC, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
+    constexpr int kStageBytes = kABytes + kBBytes;
+    constexpr int L = (BM + BN) / 64;  // load instructions per wave per stage
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave >> 1) * WTM;
+    const int wn0 = (wave & 1) * WTN;
+
+    // ---- block id -> (slice, tile row, tile col)
+    const int nbm = (int)((g.M + BM - 1) / BM);
+    const int nbn = (int)((g.N + BN - 1) / BN);
+    const int tiles = nbm * nbn;
+    const int total = gridDim.x;
+    const int lin = blockIdx.x;
+    const int q = total / kXcds, rem = total % kXcds;
+    const int xcd = lin % kXcds, loc = lin / kXcds;
+    const int id = xcd * q + (xcd < rem ? xcd : rem) + loc;
+    const int slice = id / tiles;
+    const int pid = id - slice * tiles;
+    const int per_group = kGroupM * nbn;
+    const int first_m = (pid / per_group) * kGroupM;
+    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+
+    const int64_t kbeg = (int64_t)slice * g.k_split;
+    const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
+    const int nkt = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+
+    const int64_t a_rows = A_OC ? g.K : g.M;  // storage rows of each operand
+    const int64_t b_rows = B_OC ? g.K : g.N;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, (int)(a_rows * g.lda * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.B, 0, (int)(b_rows * g.ldb * 2), kRsrcWord3);
+
+    Dma<BM, A_OC> da;
+    Dma<BN, B_OC> db;
+    da.init(wave, lane, g.lda, m0, g.M);
+    db.init(wave, lane, g.ldb, n0, g.N);
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    if (nkt > 0) {
+        // Prologue: fill the whole ring. Stages past the end of the reduction
+        // get out-of-range offsets everywhere (zeros into a free slot), so every
+        // iteration below issues and waits for the same number of loads.
+#pragma unroll
+        for (int s = 0; s < kStages; ++s) {
+            char* st = smem + s * kStageBytes;
+            da.template issue<0, Dma<BM, A_OC>::kInstr>(ra, st, kbeg + s * kBK, kend, g.lda, wave);
+            db.template issue<0, Dma<BN, B_OC>::kInstr>(rb, st + kABytes, kbeg + s * kBK, kend, g.ldb, wave);
+        }
+        waitcnt<(kStages - 1) * L, 0>();
+        __builtin_amdgcn_s_barrier();
+
+        bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa0[i] = fragment<BM, A_OC>(smem, wm0 + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb0[j] = fragment<BN, B_OC>(smem + kABytes, wn0 + j * 32, 0, lane);
+
+        constexpr int LA = Dma<BM, A_OC>::kInstr;
+        for (int t = 0; t < nkt; ++t) {
+            const char* st = smem + (t % kStages) * kStageBytes;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa1[i] = fragment<BM, A_OC>(st, wm0 + i * 32, 1, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb1[j] = fragment<BN, B_OC>(st + kABytes, wn0 + j * 32, 1, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // stage t is fully read by this wave; stage t + 1 must have landed
+            waitcnt<(kStages - 2) * L, 0>();
+            __builtin_amdgcn_s_barrier();
+            const char* nx = smem + ((t + 1) % kStages) * kStageBytes;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa0[i] = fragment<BM, A_OC>(nx, wm0 + i * 32, 0, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb0[j] = fragment<BN, B_OC>(nx + kABytes, wn0 + j * 32, 0, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            // second MFMA step of stage t; the loads of stage t + 4 (into the slot
+            // of stage t, free since the barrier) are spread between its rows
+            char* slot = smem + (t % kStages) * kStageBytes;
+            const int64_t k0 = kbeg + (int64_t)(t + kStages) * kBK;
+#define FCP_STEP1_ROW(I)                                                                   \
+    if constexpr ((I) < TM) {                                                              \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[I][j] =                         \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[I], acc[I][j], 0, 0, 0);   \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+        constexpr int lo = ((I) * L + TM - 1) / TM, hi = (((I) + 1) * L + TM - 1) / TM;   \
+        da.template issue<lo, hi>(ra, slot, k0, kend, g.lda, wave);                        \
+        db.template issue<lo - LA, hi - LA>(rb, slot + kABytes, k0, kend, g.ldb, wave);    \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+    }
+            FCP_STEP1_ROW(0)
+            FCP_STEP1_ROW(1)
+            FCP_STEP1_ROW(2)
+            FCP_STEP1_ROW(3)
+#undef FCP_STEP1_ROW
+        }
+        waitcnt<0, 0>();  // drain the trailing (out-of-range) loads
+    }
+
+    // ---- epilogue: lane holds C[m][n .. n+3] per 32x32 block and group
+    const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm0 + i * 32 + lr;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int64_t n = n0 + wn0 + j * 32 + grp * 8 + lk * 4;
+                if (n >= g.N) continue;
+                const float v0 = acc[i][j][grp * 4 + 0], v1 = acc[i][j][grp * 4 + 1];
+                const float v2 = acc[i][j][grp * 4 + 2], v3 = acc[i][j][grp * 4 + 3];
+                if (OUT_F32) {
+                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
+                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+                } else {
+                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
+                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 8-wave ping-pong variant, 256 x 256 block tile (512 threads, 2 waves/SIMD).
+//
+// Waves 0-3 (group 0) compute output rows 0-127 of the tile, waves 4-7
+// (group 1) rows 128-255; inside a group the 4 waves form a 2 x 2 grid of
+// 64 x 128 wave tiles. Time is cut into phases separated by workgroup
+// barriers. In each phase one group reads its operand fragments of a stage
+// from LDS (and issues its half of the loads of a later stage) while the
+// other group runs the MFMAs of the stage it read in the previous phase:
+//
+//   phase     0     1     2     3    ...   2t     2t+1
+//   group 0   M(0)  C(0)  M(1)  C(1) ...   M(t)   C(t)
+//   group 1   -     M(0)  C(0)  M(1) ...   C(t-1) M(t)
+//
+// so each SIMD always holds one wave with MFMA work. A stage holds KS x 16
+// reduction values; the ring has S slots (KS = 3, S = 3: 48-value stages,
+// 144 KB). Group 0 loads the A operand of every stage and group 1 the B
+// operand; M(t) requests stage t + S - 1 into the slot of stage t - 1, which
+// both groups finished reading before the barrier that opens the phase.
+// Every wave issues the same number of loads in every M phase (out-of-range
+// offsets past the end of the reduction), so "at most S - 2 stages of loads
+// in flight" before every barrier is exactly "the stage the next M phase
+// reads has landed".
+
+// reduction-contiguous LDS tile row of BKP values: 16-byte chunk c of row i
+template <int BKP>
+__device__ __forceinline__ uint32_t rc_slot_k(int i, int c) {
+    if constexpr (BKP == 32)
+        return i * 64 + ((c ^ ((i >> 2) & 3)) << 4);
+    else  // 48 values = 6 chunks: flip the chunk's low bit on alternate 8-row groups
+        return i * (BKP * 2) + ((c ^ ((i >> 3) & 1)) << 4);
+}
+
+// loads of one operand tile (256 rows x BKP reduction values) shared by 4 waves
+template <bool OC, int BKP>
+struct DmaPP {
+    static constexpr int R = 256;
+    static constexpr int kInstr = R * BKP * 2 / 1024 / 4;  // per wave
+    uint32_t base[kInstr];
+    int kk[kInstr];
+
+    __device__ __forceinline__ void init(int wq, int lane, int64_t ld, int64_t row0, int64_t rows) {
+#pragma unroll
+        for (int j = 0; j < kInstr; ++j) {
+            const int p = (wq * kInstr + j) * 64 + lane;  // 16-byte slot in the tile
+            if (!OC) {
+                constexpr int CPR = BKP / 8;
+                const int i = p / CPR, pc = p % CPR;
+                int c;
+                if constexpr (BKP == 32)
+                    c = pc ^ ((i >> 2) & 3);
+                else
+                    c = pc ^ ((i >> 3) & 1);
+                kk[j] = 8 * c;
+                base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
+            } else {
+                constexpr int CPR = R / 8;
+                const int k = p / CPR;
+                const int c = (p % CPR) ^ ((k & 3) << 2);
+                kk[j] = k;
+                base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* region, int64_t k0, int64_t kend,
+                                          int64_t ld, int wq) const {
+        const uint32_t step = OC ? (uint32_t)(k0 * ld * 2) : (uint32_t)(k0 * 2);
+#pragma unroll
+        for (int j = 0; j < kInstr; ++j) {
+            const uint32_t off = (base[j] == kOOB || k0 + kk[j] >= kend) ? kOOB : base[j] + step;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wq * kInstr + j) * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
+    }
+};
+
+template <bool OC, int BKP>
+__device__ __forceinline__ bf16x8 fragment_pp(const char* region, int r0, int ks, int lane) {
+    if constexpr (!OC) {
+        const int i = r0 + (lane & 31);
+        const int c = ks * 2 + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot_k<BKP>(i, c));
+    } else {
+        return fragment<256, true>(region, r0, ks, lane);
+    }
+}
+
+template <bool A_OC, bool B_OC, bool OUT_F32, int KS>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int TM = 2, TN = 4;  // 64 x 128 wave tile
+    constexpr int BKP = 16 * KS;   // reduction values per stage
+    constexpr int S = KS == 2 ? 4 : 3;
+    constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
+    constexpr int kStageBytes = kABytes + kBBytes;
+    constexpr int kLoads = DmaPP<A_OC, BKP>::kInstr;  // per wave per M phase (same for B)
+    static_assert(DmaPP<A_OC, BKP>::kInstr == DmaPP<B_OC, BKP>::kInstr, "balanced loaders");
+    constexpr int kInFlight = (S - 2) * kLoads;
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int q = wave & 3;
+    const int wm0 = grp * 128 + (q >> 1) * 64;
+    const int wn0 = (q & 1) * 128;
+
+    const int nbm = (int)((g.M + BM - 1) / BM);
+    const int nbn = (int)((g.N + BN - 1) / BN);
+    const int tiles = nbm * nbn;
+    const int total = gridDim.x;
+    const int lin = blockIdx.x;
+    const int qq = total / kXcds, rem = total % kXcds;
+    const int xcd = lin % kXcds, loc = lin / kXcds;
+    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
+    const int slice = id / tiles;
+    const int pid = id - slice * tiles;
+    const int per_group = kGroupM * nbn;
+    const int first_m = (pid / per_group) * kGroupM;
+    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+
+    const int64_t kbeg = (int64_t)slice * g.k_split;
+    const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
+    const int nkt = kend > kbeg ? (int)((kend - kbeg + BKP - 1) / BKP) : 0;
+
+    const bool loadA = grp == 0;
+    const int64_t rows_st = loadA ? (A_OC ? g.K : g.M) : (B_OC ? g.K : g.N);
+    const int64_t ld = loadA ? g.lda : g.ldb;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(loadA ? g.A : g.B), 0, (int)(rows_st * ld * 2), kRsrcWord3);
+    DmaPP<A_OC, BKP> da;
+    DmaPP<B_OC, BKP> db;
+    if (loadA)
+        da.init(q, lane, g.lda, m0, g.M);
+    else
+        db.init(q, lane, g.ldb, n0, g.N);
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // stage s into its ring slot; A half from group 0, B half from group 1
+    auto issue_stage = [&](int s) {
+        char* st = smem + (s % S) * kStageBytes;
+        const int64_t k0 = kbeg + (int64_t)s * BKP;
+        if (loadA)
+            da.issue(rs, st, k0, kend, g.lda, q);
+        else
+            db.issue(rs, st + kABytes, k0, kend, g.ldb, q);
+    };
+
+    if (nkt > 0) {
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s) issue_stage(s);
+        waitcnt<kInFlight, 0>();
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1) {  // group 1 starts one phase later
+            waitcnt<kInFlight, 0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        bf16x8 fa[KS][TM], fb[KS][TN];
+        for (int t = 0; t < nkt; ++t) {
+            // ---- M(t): fragments of stage t, loads of stage t + S - 1
+            const char* st = smem + (t % S) * kStageBytes;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[ks][i] = fragment_pp<A_OC, BKP>(st, wm0 + i * 32, ks, lane);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[ks][j] = fragment_pp<B_OC, BKP>(st + kABytes, wn0 + j * 32, ks, lane);
+            }
+            issue_stage(t + S - 1);
+            waitcnt<kInFlight, 0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- C(t)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            waitcnt<kInFlight, 0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        if (grp == 0) {  // matching trailing phase
+            waitcnt<kInFlight, 0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        waitcnt<0, 0>();  // drain the trailing (out-of-range) loads
+    }
+
+    const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm0 + i * 32 + lr;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int64_t n = n0 + wn0 + j * 32 + gq * 8 + lk * 4;
+                if (n >= g.N) continue;
+                const float v0 = acc[i][j][gq * 4 + 0], v1 = acc[i][j][gq * 4 + 1];
+                const float v2 = acc[i][j][gq * 4 + 2], v3 = acc[i][j][gq * 4 + 3];
+                if (OUT_F32) {
+                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
+                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+                } else {
+                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
+                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                }
+            }
+        }
+    }
+}
+
+using KernelFn = void (*)(GemmArgs);
+struct Entry {
+    KernelFn fn;
+    const char* name;
+};
+
+#define FCP_K(BM, BN, AOC, BOC, F32) \
+    Entry { gemm_pipe_kernel<BM, BN, AOC, BOC, F32>, "gemm_pipe_kernel<" #BM ", " #BN ", " #AOC ", " #BOC ", " #F32 ">" }
+#define FCP_LAYOUTS(BM, BN, F32)                                                                 \
+    FCP_K(BM, BN, false, false, F32), FCP_K(BM, BN, false, true, F32), FCP_K(BM, BN, true, false, F32), \
+        FCP_K(BM, BN, true, true, F32)
+#define FCP_TILE(BM, BN) FCP_LAYOUTS(BM, BN, false), FCP_LAYOUTS(BM, BN, true)
+
+// [tile][out_f32][a_oc][b_oc], tiles in the order of kTiles
+const Entry kPipe[kNumTiles * 8] = {
+    FCP_TILE(256, 256),
+    FCP_TILE(256, 128),
+    FCP_TILE(128, 256),
+    FCP_TILE(128, 128),
+};
+
+#define FCPP_K(AOC, BOC, F32, KS) \
+    Entry { gemm_pp_kernel<AOC, BOC, F32, KS>, "gemm_pp_kernel<" #AOC ", " #BOC ", " #F32 ", " #KS ">" }
+#define FCPP_ALL(KS)                                                                                            \
+    FCPP_K(false, false, false, KS), FCPP_K(false, true, false, KS), FCPP_K(true, false, false, KS),            \
+        FCPP_K(true, true, false, KS), FCPP_K(false, false, true, KS), FCPP_K(false, true, true, KS),           \
+        FCPP_K(true, false, true, KS), FCPP_K(true, true, true, KS)
+// [depth: 0 -> 48-value stages, 1 -> 32-value stages][out_f32][a_oc][b_oc]
+const Entry kPingPong[2][8] = {{FCPP_ALL(3)}, {FCPP_ALL(2)}};
+
+const Entry& pipe_entry(int tile, bool a_oc, bool b_oc, bool out_f32) {
+    return kPipe[tile * 8 + (out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
+}
+
+}  // namespace
+
+const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32) {
+    return pipe_entry(tile, a_oc, b_oc, out_f32).name;
+}
+
+const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32) {
+    return kPingPong[depth][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)].name;
+}
+
+hipError_t launch_gemm_pingpong(int depth, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+                                hipStream_t stream) {
+    const int64_t blocks = ((args.M + 255) / 256) * ((args.N + 255) / 256) * (int64_t)args.splits;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kPingPong[depth][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)].fn, dim3((unsigned)blocks),
+                       dim3(512), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_pipe(int tile, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+                            hipStream_t stream) {
+    const TileCfg& t = kTiles[tile];
+    const int64_t blocks = ((args.M + t.bm - 1) / t.bm) * ((args.N + t.bn - 1) / t.bn) * (int64_t)args.splits;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pipe_entry(tile, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       args);
+    return hipGetLastError();
+}
+
+}  // namespace fcs

@@ -169,7 +169,7 @@ def fc_plan_describe(op: int, M: int, K: int, N: int, x_order: int = ROW, w_orde
     buf = ctypes.create_string_buffer(512)
     _check(lib().fc_plan_describe(op, M, K, N, x_order, w_order, out_dtype, buf, 512), "fc_plan_describe")
     text = buf.value.decode()
-    d = dict(re.findall(r"(\w+)=(gemm_bf16_kernel<[^>]*>|\S+)", text))
+    d = dict(re.findall(r"(\w+)=(gemm_\w+_kernel<[^>]*>|\S+)", text))
     for k in ("plan", "split", "copy", "ws"):
         d[k] = int(d[k])
     return d
