@@ -33,6 +33,34 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "sharded_fc_layer_amd", "csrc", f)
+                  for f in ("gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; counter figures taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or None
+    when none were taken for it or the kernel sources changed since."""
+    import json as _json
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = _json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 WORKLOAD_NAMES = {
     1: "single_fc_256x512x2048",
@@ -55,6 +83,8 @@ def parse():
     p.add_argument("--plans", default=None,
                    help="plan file: loaded if it exists (no tuning in this run), else written after tuning")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one plain 1 GiB device copy (a known-size reference for HBM counters)")
     return p.parse_args()
 
 
@@ -149,9 +179,11 @@ def run_per_launch(layers, steps, torch, F):
         desc = F.fc_plan_describe(op, g.M, g.K, g.N)
         key = desc["kernel"]
         single = desc["split"] == 1 and desc["copy"] == 0
-        e = out.setdefault(key, {"ms": [], "flops": [], "single_launch": True})
+        e = out.setdefault(key, {"ms": [], "flops": [], "bytes": [], "single_launch": True})
         e["ms"].append(a.elapsed_time(b))
         e["flops"].append(g.flops)
+        # compulsory HBM bytes: both bf16 inputs once, the bf16 output once
+        e["bytes"].append(2 * (g.M * g.K + g.K * g.N + g.M * g.N))
         e["single_launch"] = e["single_launch"] and single
     return out
 
@@ -245,6 +277,13 @@ def main():
     t = time.perf_counter()
     layers = make_layers(args.workload, torch, F, I, host_inputs=True)
     log(f"inputs resident ({time.perf_counter() - t:.1f} s)")
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 1 GiB read + 1 GiB write")
     tune_s = 0.0
     if args.plans and os.path.exists(args.plans):
         F.fc_plans_load(args.plans)
@@ -275,9 +314,11 @@ def main():
     d_avg_flops = float(np.mean(drec["flops"]))
     achieved = d_avg_flops / (d_avg_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dname,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dname, WORKLOAD_NAMES[args.workload]), "kernel": dname,
                 "launches": len(drec["ms"]), "avg_launch_us": round(d_avg_ms * 1e3, 2),
                 "avg_gflop_per_launch": round(d_avg_flops / 1e9, 3),
+                "algorithmic_bytes_per_launch": int(np.mean(drec["bytes"])),
                 "single_launch_plans": drec["single_launch"]}
     per_kernel = {k: {"launches": len(v["ms"]), "avg_us": round(float(np.mean(v["ms"])) * 1e3, 2),
                       "tflops": round(float(np.sum(v["flops"]) / (np.sum(v["ms"]) / 1e3) / 1e12), 1)}
@@ -308,6 +349,7 @@ def main():
         "per_kernel": per_kernel,
         "plans": plans_of(layers, F),
         "tune_s": round(tune_s, 2),
+        "kernel_source_hash": kernel_source_hash(),
         "device": props.name,
     }
 

@@ -3,9 +3,14 @@
 Reads a rocprofv3 rocpd database (<name>_results.db) and prints, per kernel
 (optionally per kernel and grid size), the dispatch count and the average,
 minimum, maximum and total duration; for counter runs (--pmc) it prints the
-per-dispatch averages of each counter. Usage:
+per-dispatch averages of each counter. With --traffic it combines a
+FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per launch of each kernel,
+scaled by what the same counters read for a plain copy of known size.
+Usage:
 
   python -m sharded_fc_layer_amd.rocprof_summary RESULTS.db [--by-grid] [--pmc]
+  python -m sharded_fc_layer_amd.rocprof_summary --traffic FETCH.db WRITE.db \
+      --copy-kernel REGEX --copy-bytes N [--json OUT --workload NAME --source-hash H]
 """
 from __future__ import annotations
 
@@ -60,13 +65,69 @@ def summarize_pmc(db: str, out=sys.stdout):
             out.write(f"{k:<66} {c:<22} {len(vals):>10} {sum(vals) / len(vals):>18.1f}\n")
 
 
+def counter_per_dispatch(db: str, counter: str):
+    """{kernel: [value per dispatch]} for one counter (summed over dimensions)."""
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    cols = [d[0] for d in cur.execute("select * from counters_collection limit 1").description]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    per = defaultdict(lambda: defaultdict(float))
+    for kname, cname, val, disp in cur.execute(
+            f"select {name_col}, counter_name, value, dispatch_id from counters_collection"):
+        if cname == counter:
+            per[short(kname)][disp] += float(val)
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def traffic(fetch_db: str, write_db: str, copy_kernel: str, copy_bytes: int, out=sys.stdout):
+    """HBM bytes per launch, each counter scaled by its reading on the copy."""
+    fetch = counter_per_dispatch(fetch_db, "FETCH_SIZE")
+    write = counter_per_dispatch(write_db, "WRITE_SIZE")
+    pat = re.compile(copy_kernel)
+    cf = [v for k, vs in fetch.items() if pat.search(k) for v in vs]
+    cw = [v for k, vs in write.items() if pat.search(k) for v in vs]
+    if not cf or not cw:
+        raise SystemExit(f"copy kernel {copy_kernel!r} not found in the counter runs")
+    # counters are in KiB per dispatch; the copy reads and writes copy_bytes
+    f_scale = copy_bytes / (1024.0 * max(cf))
+    w_scale = copy_bytes / (1024.0 * max(cw))
+    res = {"copy_kernel": copy_kernel, "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
+    out.write(f"copy calibration: FETCH_SIZE {max(cf):.0f} KiB, WRITE_SIZE {max(cw):.0f} KiB for "
+              f"{copy_bytes / 2**30:.3f} GiB each -> scale fetch {f_scale:.4f}, write {w_scale:.4f}\n")
+    out.write(f"{'kernel':<66} {'launches':>8} {'fetch_MB':>10} {'write_MB':>10} {'hbm_MB/launch':>14}\n")
+    for k in sorted(set(fetch) & set(write)):
+        if pat.search(k):
+            continue
+        f = sum(fetch[k]) / len(fetch[k]) * 1024 * f_scale
+        w = sum(write[k]) / len(write[k]) * 1024 * w_scale
+        res["kernels"][k] = {"launches": len(fetch[k]), "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+                             "hbm_bytes_per_launch": f + w}
+        out.write(f"{k:<66} {len(fetch[k]):>8} {f / 1e6:>10.1f} {w / 1e6:>10.1f} {(f + w) / 1e6:>14.1f}\n")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("db")
+    ap.add_argument("db", nargs="?")
     ap.add_argument("--by-grid", action="store_true")
     ap.add_argument("--pmc", action="store_true")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--copy-kernel", default="elementwise")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--json", default=None)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--source-hash", default=None)
     a = ap.parse_args()
-    if a.pmc:
+    if a.traffic:
+        res = traffic(a.traffic[0], a.traffic[1], a.copy_kernel, a.copy_bytes)
+        if a.json:
+            import json
+            res["workload"] = a.workload
+            res["source_hash"] = a.source_hash
+            with open(a.json, "w") as f:
+                json.dump(res, f, indent=1)
+    elif a.pmc:
         summarize_pmc(a.db)
     else:
         summarize(a.db, a.by_grid)
