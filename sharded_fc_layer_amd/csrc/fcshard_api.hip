@@ -36,8 +36,9 @@ namespace {
 constexpr int kSplits[] = {1, 2, 4};
 constexpr int kNumSplits = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
-// 0: pipelined, 1: simple, 8-wave ping-pong with 2: 48-, 3: 32-, 4: 64-value stages
-constexpr int kNumFamilies = 5;
+// 0: pipelined, 1: simple, 8-wave ping-pong with 2: 48-, 3: 32-, 4: 64-value stages,
+// 5: 32-value stages and one barrier per stage; 6, 7: 3 and 5 with 16x16x32 MFMAs
+constexpr int kNumFamilies = 8;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
 constexpr int kMaxDevices = 64;
@@ -46,7 +47,7 @@ struct Plan {
     int tile;
     int split;   // number of reduction slices requested
     int copy;    // bit mask
-    int family;  // 0 pipelined, 1 simple, 2/3/4 ping-pong (48/32/64-value stages)
+    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants
 };
 
 Plan decode_plan(int id) {

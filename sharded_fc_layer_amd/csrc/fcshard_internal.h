@@ -51,7 +51,8 @@ const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32);
 
 // Enqueue the 8-wave ping-pong GEMM (256 x 256 tile; same requirements as
 // launch_gemm_pipe). depth 0: 48-value reduction stages, 1: 32-value stages,
-// 2: 64-value stages (gemm_pp64_kernel).
+// 2: 64-value stages (gemm_pp64_kernel), 3: 32-value stages with one
+// barrier per stage (gemm_pp1b_kernel), 4 and 5: 1 and 3 with 16x16x32 MFMAs.
 hipError_t launch_gemm_pingpong(int depth, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                                 hipStream_t stream);
 const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32);

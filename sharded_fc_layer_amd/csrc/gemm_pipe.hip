@@ -367,11 +367,91 @@ __device__ __forceinline__ bf16x8 fragment_pp(const char* region, int r0, int ks
     }
 }
 
-template <bool A_OC, bool B_OC, bool OUT_F32, int KS>
+// accumulator type and MFMA of one output block: 32 x 32 x 16 or 16 x 16 x 32
+template <int MF>
+struct AccT;
+template <>
+struct AccT<32> {
+    typedef f32x16 type;
+    static constexpr int n = 16;
+};
+template <>
+struct AccT<16> {
+    typedef f32x4 type;
+    static constexpr int n = 4;
+};
+
+template <int MF>
+__device__ __forceinline__ typename AccT<MF>::type mfma_bf16(bf16x8 a, bf16x8 b, typename AccT<MF>::type c) {
+    if constexpr (MF == 32)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// MFMA operand of an MF-row block at r0, reduction step ks of a BKP-value stage.
+// 16 x 16 x 32: lane l holds block row l % 16 and reduction values
+// 32 ks + 8 (l / 16) .. +7; for output-contiguous tiles the 16-lane group g
+// reads rows 32 ks + 8 g (+4) with two ds_read_b64_tr_b16.
+template <bool OC, int BKP, int MF>
+__device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks, int lane) {
+    if constexpr (MF == 32) {
+        return fragment_pp<OC, BKP>(region, r0, ks, lane);
+    } else if constexpr (!OC) {
+        const int i = r0 + (lane & 15);
+        const int c = ks * 4 + (lane >> 4);
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot_k<BKP>(i, c));
+    } else {
+        const int g = lane >> 4, j = lane & 15;
+        const int col = r0 + 4 * (j & 3);
+        const int k = ks * 32 + 8 * g + (j >> 2);
+        const int c = col >> 3, half = (col & 7) << 1;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(region + oc_slot<256>(k, c) + half));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(region + oc_slot<256>(k + 4, c) + half));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// epilogue of one wave tile: rows m0 + wm0 .., columns n0 + wn0 ..; each lane
+// holds 4 consecutive output columns of one row per block
+template <int MF, int TM, int TN, bool OUT_F32>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t m0, int64_t n0, int wm0, int wn0,
+                                           int lane, const typename AccT<MF>::type (&acc)[TM][TN]) {
+    constexpr int GR = MF == 32 ? 4 : 1;  // 4-column groups per lane per block
+    const int lr = lane & (MF - 1), lk = MF == 32 ? (lane >> 5) : (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm0 + i * MF + lr;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int gq = 0; gq < GR; ++gq) {
+                const int64_t n = n0 + wn0 + j * MF + gq * 8 + lk * 4;
+                if (n >= g.N) continue;
+                const float v0 = acc[i][j][gq * 4 + 0], v1 = acc[i][j][gq * 4 + 1];
+                const float v2 = acc[i][j][gq * 4 + 2], v3 = acc[i][j][gq * 4 + 3];
+                if (OUT_F32) {
+                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
+                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+                } else {
+                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
+                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                }
+            }
+        }
+    }
+}
+
+template <bool A_OC, bool B_OC, bool OUT_F32, int KS, int MF>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256;
-    constexpr int TM = 2, TN = 4;  // 64 x 128 wave tile
-    constexpr int BKP = 16 * KS;   // reduction values per stage
+    constexpr int TM = 64 / MF, TN = 128 / MF;  // 64 x 128 wave tile
+    constexpr int BKP = 16 * KS;                // reduction values per stage
+    constexpr int KSM = MF == 32 ? KS : KS / 2;  // MFMA reduction steps per stage
     constexpr int S = KS == 2 ? 4 : 3;
     constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
     constexpr int kStageBytes = kABytes + kBBytes;
@@ -422,13 +502,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     else
         db.init(q, lane, g.ldb, n0, g.N);
 
-    f32x16 acc[TM][TN];
+    typename AccT<MF>::type acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < AccT<MF>::n; ++e) acc[i][j][e] = 0.0f;
 
     // stage s into its ring slot; A half from group 0, B half from group 1
     auto issue_stage = [&](int s) {
@@ -449,16 +529,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
             waitcnt<kInFlight, 0>();
             __builtin_amdgcn_s_barrier();
         }
-        bf16x8 fa[KS][TM], fb[KS][TN];
+        bf16x8 fa[KSM][TM], fb[KSM][TN];
         for (int t = 0; t < nkt; ++t) {
             // ---- M(t): fragments of stage t, loads of stage t + S - 1
             const char* st = smem + (t % S) * kStageBytes;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KSM; ++ks) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) fa[ks][i] = fragment_pp<A_OC, BKP>(st, wm0 + i * 32, ks, lane);
+                for (int i = 0; i < TM; ++i) fa[ks][i] = fragment_mf<A_OC, BKP, MF>(st, wm0 + i * MF, ks, lane);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) fb[ks][j] = fragment_pp<B_OC, BKP>(st + kABytes, wn0 + j * 32, ks, lane);
+                for (int j = 0; j < TN; ++j)
+                    fb[ks][j] = fragment_mf<B_OC, BKP, MF>(st + kABytes, wn0 + j * MF, ks, lane);
             }
             issue_stage(t + S - 1);
             waitcnt<kInFlight, 0>();
@@ -466,12 +547,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             // ---- C(t)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KSM; ++ks)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma_bf16<MF>(fb[ks][j], fa[ks][i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
             waitcnt<kInFlight, 0>();
             __builtin_amdgcn_s_barrier();
@@ -483,29 +563,153 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
         waitcnt<0, 0>();  // drain the trailing (out-of-range) loads
     }
 
-    const int lr = lane & 31, lk = lane >> 5;
+    store_tile<MF, TM, TN, OUT_F32>(g, slice, m0, n0, wm0, wn0, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// 8-wave ping-pong with one barrier per stage (ping-pong-1b), 256 x 256.
+//
+// Same tiles, ring (4 slots of 32-value stages) and load split as
+// gemm_pp_kernel, but the interval between two barriers holds one stage of
+// both groups with their phases in opposite order:
+//
+//   interval t:   group 0: M(t) then C(t)      group 1: C(t - 1) then M(t)
+//
+// On each SIMD the group-1 wave computes while the group-0 wave reads, then
+// the group-0 wave computes (as soon as its own fragments are in registers:
+// no barrier needed) while the group-1 wave reads. A barrier is only needed
+// where data crosses waves: stage t + 1 must have landed (every wave waits
+// for its own loads first) and stage t - 1 must be free before M(t) refills
+// its slot. That halves the barriers per MFMA compared with gemm_pp_kernel.
+template <bool A_OC, bool B_OC, bool OUT_F32, int MF>
+__global__ __launch_bounds__(512) void gemm_pp1b_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int TM = 64 / MF, TN = 128 / MF;
+    constexpr int BKP = 32, S = 4;
+    constexpr int KS = MF == 32 ? 2 : 1;  // MFMA reduction steps per stage
+    constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
+    constexpr int kStageBytes = kABytes + kBBytes;
+    constexpr int kLoads = DmaPP<A_OC, BKP>::kInstr;
+    constexpr int kInFlight = (S - 2) * kLoads;
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int q = wave & 3;
+    const int wm0 = grp * 128 + (q >> 1) * 64;
+    const int wn0 = (q & 1) * 128;
+
+    const int nbm = (int)((g.M + BM - 1) / BM);
+    const int nbn = (int)((g.N + BN - 1) / BN);
+    const int tiles = nbm * nbn;
+    const int total = gridDim.x;
+    const int lin = blockIdx.x;
+    const int qq = total / kXcds, rem = total % kXcds;
+    const int xcd = lin % kXcds, loc = lin / kXcds;
+    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
+    const int slice = id / tiles;
+    const int pid = id - slice * tiles;
+    const int per_group = kGroupM * nbn;
+    const int first_m = (pid / per_group) * kGroupM;
+    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+
+    const int64_t kbeg = (int64_t)slice * g.k_split;
+    const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
+    const int nkt = kend > kbeg ? (int)((kend - kbeg + BKP - 1) / BKP) : 0;
+
+    const bool loadA = grp == 0;
+    const int64_t rows_st = loadA ? (A_OC ? g.K : g.M) : (B_OC ? g.K : g.N);
+    const int64_t ld = loadA ? g.lda : g.ldb;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(loadA ? g.A : g.B), 0, (int)(rows_st * ld * 2), kRsrcWord3);
+    DmaPP<A_OC, BKP> da;
+    DmaPP<B_OC, BKP> db;
+    if (loadA)
+        da.init(q, lane, g.lda, m0, g.M);
+    else
+        db.init(q, lane, g.ldb, n0, g.N);
+
+    typename AccT<MF>::type acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm0 + i * 32 + lr;
-        if (m >= g.M) continue;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int64_t n = n0 + wn0 + j * 32 + gq * 8 + lk * 4;
-                if (n >= g.N) continue;
-                const float v0 = acc[i][j][gq * 4 + 0], v1 = acc[i][j][gq * 4 + 1];
-                const float v2 = acc[i][j][gq * 4 + 2], v3 = acc[i][j][gq * 4 + 3];
-                if (OUT_F32) {
-                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
-                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
-                } else {
-                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
-                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                }
-            }
-        }
+            for (int e = 0; e < AccT<MF>::n; ++e) acc[i][j][e] = 0.0f;
+
+#define FCP1B_ISSUE(SIDX)                                                                      \
+    {                                                                                          \
+        char* st_ = smem + ((SIDX) % S) * kStageBytes;                                         \
+        const int64_t k0_ = kbeg + (int64_t)(SIDX) * BKP;                                      \
+        if (loadA)                                                                             \
+            da.issue(rs, st_, k0_, kend, g.lda, q);                                            \
+        else                                                                                   \
+            db.issue(rs, st_ + kABytes, k0_, kend, g.ldb, q);                                  \
     }
+#define FCP1B_M(T)                                                                                       \
+    {                                                                                                    \
+        const char* st_ = smem + ((T) % S) * kStageBytes;                                                \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                              \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[ks][i] =                                   \
+                fragment_mf<A_OC, BKP, MF>(st_, wm0 + i * MF, ks, lane);                                 \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[ks][j] =                                   \
+                fragment_mf<B_OC, BKP, MF>(st_ + kABytes, wn0 + j * MF, ks, lane);                       \
+        }                                                                                                \
+        FCP1B_ISSUE((T) + S - 1)                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                               \
+    }
+#define FCP1B_C()                                                                                        \
+    {                                                                                                    \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) _Pragma("unroll") for (int i = 0; i < TM; ++i) \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                                   \
+                mfma_bf16<MF>(fb[ks][j], fa[ks][i], acc[i][j]);                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                               \
+    }
+#define FCP1B_SYNC()                 \
+    {                                \
+        waitcnt<kInFlight, 0>();     \
+        __builtin_amdgcn_s_barrier(); \
+        __builtin_amdgcn_sched_barrier(0); \
+    }
+
+    if (nkt > 0) {
+        FCP1B_ISSUE(0)
+        FCP1B_ISSUE(1)
+        FCP1B_ISSUE(2)
+        FCP1B_SYNC()
+        bf16x8 fa[KS][TM], fb[KS][TN];
+        if (loadA) {
+            for (int t = 0; t < nkt; ++t) {
+                FCP1B_M(t)
+                FCP1B_C()
+                FCP1B_SYNC()
+            }
+            FCP1B_SYNC()  // the interval in which group 1 finishes its last stage
+        } else {
+            FCP1B_M(0)
+            FCP1B_SYNC()
+            for (int t = 1; t < nkt; ++t) {
+                FCP1B_C()
+                FCP1B_M(t)
+                FCP1B_SYNC()
+            }
+            FCP1B_C()
+            FCP1B_SYNC()
+        }
+        waitcnt<0, 0>();
+    }
+#undef FCP1B_ISSUE
+#undef FCP1B_M
+#undef FCP1B_C
+#undef FCP1B_SYNC
+
+    store_tile<MF, TM, TN, OUT_F32>(g, slice, m0, n0, wm0, wn0, lane, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,14 +967,17 @@ const Entry kPipe[kNumTiles * 8] = {
     FCP_TILE(128, 128),
 };
 
-#define FCPP_K(AOC, BOC, F32, KS) \
-    Entry { gemm_pp_kernel<AOC, BOC, F32, KS>, "gemm_pp_kernel<" #AOC ", " #BOC ", " #F32 ", " #KS ">" }
-#define FCPP_ALL(KS)                                                                                            \
-    FCPP_K(false, false, false, KS), FCPP_K(false, true, false, KS), FCPP_K(true, false, false, KS),            \
-        FCPP_K(true, true, false, KS), FCPP_K(false, false, true, KS), FCPP_K(false, true, true, KS),           \
-        FCPP_K(true, false, true, KS), FCPP_K(true, true, true, KS)
-// [depth: 0 -> 48-value stages, 1 -> 32-value stages][out_f32][a_oc][b_oc]
-const Entry kPingPong[2][8] = {{FCPP_ALL(3)}, {FCPP_ALL(2)}};
+#define FCPP_K(AOC, BOC, F32, KS, MF)                                                              \
+    Entry {                                                                                        \
+        gemm_pp_kernel<AOC, BOC, F32, KS, MF>,                                                     \
+            "gemm_pp_kernel<" #AOC ", " #BOC ", " #F32 ", " #KS ", " #MF ">"                       \
+    }
+#define FCPP_ALL(KS, MF)                                                                                        \
+    FCPP_K(false, false, false, KS, MF), FCPP_K(false, true, false, KS, MF), FCPP_K(true, false, false, KS, MF), \
+        FCPP_K(true, true, false, KS, MF), FCPP_K(false, false, true, KS, MF), FCPP_K(false, true, true, KS, MF), \
+        FCPP_K(true, false, true, KS, MF), FCPP_K(true, true, true, KS, MF)
+// [variant: 48-value stages, 32-value stages, 32-value stages with 16x16x32 MFMA][out_f32][a_oc][b_oc]
+const Entry kPingPong[3][8] = {{FCPP_ALL(3, 32)}, {FCPP_ALL(2, 32)}, {FCPP_ALL(2, 16)}};
 
 #define FCPP64_K(AOC, BOC, F32) \
     Entry { gemm_pp64_kernel<AOC, BOC, F32>, "gemm_pp64_kernel<" #AOC ", " #BOC ", " #F32 ">" }
@@ -779,6 +986,14 @@ const Entry kPingPong64[8] = {
     FCPP64_K(true, true, false),   FCPP64_K(false, false, true), FCPP64_K(false, true, true),
     FCPP64_K(true, false, true),   FCPP64_K(true, true, true),
 };
+
+#define FCPP1B_K(AOC, BOC, F32, MF) \
+    Entry { gemm_pp1b_kernel<AOC, BOC, F32, MF>, "gemm_pp1b_kernel<" #AOC ", " #BOC ", " #F32 ", " #MF ">" }
+#define FCPP1B_ALL(MF)                                                                                  \
+    FCPP1B_K(false, false, false, MF), FCPP1B_K(false, true, false, MF), FCPP1B_K(true, false, false, MF), \
+        FCPP1B_K(true, true, false, MF), FCPP1B_K(false, false, true, MF), FCPP1B_K(false, true, true, MF), \
+        FCPP1B_K(true, false, true, MF), FCPP1B_K(true, true, true, MF)
+const Entry kPingPong1b[2][8] = {{FCPP1B_ALL(32)}, {FCPP1B_ALL(16)}};
 
 const Entry& pipe_entry(int tile, bool a_oc, bool b_oc, bool out_f32) {
     return kPipe[tile * 8 + (out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
@@ -792,7 +1007,14 @@ const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32) {
 
 const Entry& pingpong_entry(int depth, bool a_oc, bool b_oc, bool out_f32) {
     const int i = (out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0);
-    return depth == 2 ? kPingPong64[i] : kPingPong[depth][i];
+    switch (depth) {
+        case 0: return kPingPong[0][i];
+        case 1: return kPingPong[1][i];
+        case 2: return kPingPong64[i];
+        case 3: return kPingPong1b[0][i];
+        case 4: return kPingPong[2][i];
+        default: return kPingPong1b[1][i];
+    }
 }
 
 const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32) {
