@@ -36,9 +36,9 @@ namespace {
 constexpr int kSplits[] = {1, 2, 4};
 constexpr int kNumSplits = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
-// 0: pipelined, 1: simple, 8-wave ping-pong with 2: 48-, 3: 32-, 4: 64-value stages,
-// 5: 32-value stages and one barrier per stage; 6, 7: 3 and 5 with 16x16x32 MFMAs
-constexpr int kNumFamilies = 8;
+// 0: 4-wave pipelined, 1: simple, 2-5: 8-wave ping-pong (256 x 256), variant
+// = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs
+constexpr int kNumFamilies = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
 constexpr int kMaxDevices = 64;
@@ -47,7 +47,7 @@ struct Plan {
     int tile;
     int split;   // number of reduction slices requested
     int copy;    // bit mask
-    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants
+    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2)
 };
 
 Plan decode_plan(int id) {
@@ -207,7 +207,7 @@ int default_plan(const Problem& p) {
     }
     // 256x256 tiles filling the chip: the 8-wave ping-pong kernel; otherwise
     // the 4-wave pipelined kernel with the largest tile that still does
-    const int pp = encode_plan(0, 0, 0, 3);
+    const int pp = encode_plan(0, 0, 0, 4);  // two-barrier ping-pong, 16x16x32
     if (tile == 0 && plan_applies(p, decode_plan(pp))) return pp;
     const int pipe = encode_plan(tile, 0, 0, 0);
     return plan_applies(p, decode_plan(pipe)) ? pipe : encode_plan(tile, 0, 0, 1);

@@ -49,13 +49,13 @@ hipError_t launch_gemm_pipe(int tile, bool a_oc, bool b_oc, bool out_f32, const 
                             hipStream_t stream);
 const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32);
 
-// Enqueue the 8-wave ping-pong GEMM (256 x 256 tile; same requirements as
-// launch_gemm_pipe). depth 0: 48-value reduction stages, 1: 32-value stages,
-// 2: 64-value stages (gemm_pp64_kernel), 3: 32-value stages with one
-// barrier per stage (gemm_pp1b_kernel), 4 and 5: 1 and 3 with 16x16x32 MFMAs.
-hipError_t launch_gemm_pingpong(int depth, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+// Enqueue an 8-wave ping-pong GEMM (256 x 256 tile; same requirements as
+// launch_gemm_pipe). variant bit 0: one barrier per reduction stage
+// (gemm_pp1b_kernel) instead of two (gemm_pp_kernel); bit 1: 16x16x32 MFMAs
+// instead of 32x32x16.
+hipError_t launch_gemm_pingpong(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                                 hipStream_t stream);
-const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32);
+const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
 
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

@@ -293,28 +293,21 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
 //   group 0   M(0)  C(0)  M(1)  C(1) ...   M(t)   C(t)
 //   group 1   -     M(0)  C(0)  M(1) ...   C(t-1) M(t)
 //
-// so each SIMD always holds one wave with MFMA work. A stage holds KS x 16
-// reduction values; the ring has S slots (KS = 3, S = 3: 48-value stages,
-// 144 KB). Group 0 loads the A operand of every stage and group 1 the B
-// operand; M(t) requests stage t + S - 1 into the slot of stage t - 1, which
-// both groups finished reading before the barrier that opens the phase.
+// so each SIMD always holds one wave with MFMA work. A stage holds 32
+// reduction values; the ring has S = 4 slots (128 KB). Group 0 loads the A
+// operand of every stage and group 1 the B operand; M(t) requests stage
+// t + S - 1 into the slot of stage t - 1, which both groups finished reading
+// before the barrier that opens the phase.
 // Every wave issues the same number of loads in every M phase (out-of-range
 // offsets past the end of the reduction), so "at most S - 2 stages of loads
 // in flight" before every barrier is exactly "the stage the next M phase
 // reads has landed".
 
-// reduction-contiguous LDS tile row of BKP values: 16-byte chunk c of row i
-template <int BKP>
-__device__ __forceinline__ uint32_t rc_slot_k(int i, int c) {
-    if constexpr (BKP == 32)
-        return i * 64 + ((c ^ ((i >> 2) & 3)) << 4);
-    else  // 48 values = 6 chunks: flip the chunk's low bit on alternate 8-row groups
-        return i * (BKP * 2) + ((c ^ ((i >> 3) & 1)) << 4);
-}
 
 // loads of one operand tile (256 rows x BKP reduction values) shared by 4 waves
 template <bool OC, int BKP>
 struct DmaPP {
+    static_assert(BKP == 32, "32-value stages");
     static constexpr int R = 256;
     static constexpr int kInstr = R * BKP * 2 / 1024 / 4;  // per wave
     uint32_t base[kInstr];
@@ -327,11 +320,7 @@ struct DmaPP {
             if (!OC) {
                 constexpr int CPR = BKP / 8;
                 const int i = p / CPR, pc = p % CPR;
-                int c;
-                if constexpr (BKP == 32)
-                    c = pc ^ ((i >> 2) & 3);
-                else
-                    c = pc ^ ((i >> 3) & 1);
+                const int c = pc ^ ((i >> 2) & 3);
                 kk[j] = 8 * c;
                 base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
             } else {
@@ -361,7 +350,7 @@ __device__ __forceinline__ bf16x8 fragment_pp(const char* region, int r0, int ks
     if constexpr (!OC) {
         const int i = r0 + (lane & 31);
         const int c = ks * 2 + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot_k<BKP>(i, c));
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
     } else {
         return fragment<256, true>(region, r0, ks, lane);
     }
@@ -400,7 +389,7 @@ __device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks
     } else if constexpr (!OC) {
         const int i = r0 + (lane & 15);
         const int c = ks * 4 + (lane >> 4);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot_k<BKP>(i, c));
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
     } else {
         const int g = lane >> 4, j = lane & 15;
         const int col = r0 + 4 * (j & 3);
@@ -446,13 +435,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t
     }
 }
 
-template <bool A_OC, bool B_OC, bool OUT_F32, int KS, int MF>
+template <bool A_OC, bool B_OC, bool OUT_F32, int MF>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256;
     constexpr int TM = 64 / MF, TN = 128 / MF;  // 64 x 128 wave tile
-    constexpr int BKP = 16 * KS;                // reduction values per stage
-    constexpr int KSM = MF == 32 ? KS : KS / 2;  // MFMA reduction steps per stage
-    constexpr int S = KS == 2 ? 4 : 3;
+    constexpr int BKP = 32;                     // reduction values per stage
+    constexpr int KSM = MF == 32 ? 2 : 1;       // MFMA reduction steps per stage
+    constexpr int S = 4;
     constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
     constexpr int kStageBytes = kABytes + kBBytes;
     constexpr int kLoads = DmaPP<A_OC, BKP>::kInstr;  // per wave per M phase (same for B)
@@ -712,240 +701,6 @@ __global__ __launch_bounds__(512) void gemm_pp1b_kernel(GemmArgs g) {
     store_tile<MF, TM, TN, OUT_F32>(g, slice, m0, n0, wm0, wn0, lane, acc);
 }
 
-// ---------------------------------------------------------------------------
-// 8-wave ping-pong with 64-value reduction stages (ping-pong-64), 256 x 256.
-//
-// Same phase structure as gemm_pp_kernel, but a stage holds 64 reduction
-// values (128-byte LDS rows, whole cache lines per row segment) and a compute
-// phase is 32 MFMAs, which halves the number of phase switches per MFMA.
-// The ring has 2 slots (2 x 64 KB). Stage t + 1 is requested in phase 2t,
-// when both groups have finished stage t - 1 (the slot's previous contents):
-// group 0 requests the A half from its M(t) phase, group 1 the B half from
-// inside its C(t - 1) phase, between MFMAs. Every wave therefore has 8 loads
-// outstanding at the end of an even phase and must have none at the end of
-// an odd phase, which is when stage t + 1 is read next.
-//
-// Reduction-contiguous tiles: row i holds 64 values (8 chunks), chunk index
-// XOR-swizzled with (i ^ (i >> 3)) & 7. Output-contiguous tiles: as in the
-// other kernels ([k][256 columns], swizzle (k & 3) << 2, ds_read_b64_tr_b16).
-__device__ __forceinline__ uint32_t rc64_slot(int i, int c) { return i * 128 + ((c ^ ((i ^ (i >> 3)) & 7)) << 4); }
-
-template <bool OC>
-struct Dma64 {
-    // one 256 x 64 operand tile = 32 KB = 32 instructions; 8 per wave of a group.
-    // 32-bit byte offsets (operands are < 2 GiB): lane part in VGPRs, the rest uniform.
-    uint32_t base;  // RC: (row0 + lane/8) * ld * 2;  OC: ((lane/32) * ld + row0) * 2
-    int rem;        // RC: rows - row0 - lane/8;      OC: rows - row0
-    uint32_t ld2;   // bytes per storage row
-    int lane;
-
-    __device__ __forceinline__ void init(int lane_, int64_t ld, int64_t row0, int64_t rows) {
-        lane = lane_;
-        ld2 = (uint32_t)(ld * 2);
-        if (!OC) {
-            base = (uint32_t)((row0 + (lane >> 3)) * ld * 2);
-            rem = (int)(rows - row0 - (lane >> 3));
-        } else {
-            base = (uint32_t)(((lane >> 5) * ld + row0) * 2);
-            rem = (int)(rows - row0);
-        }
-    }
-
-    // instruction j of wave q for the stage starting at k0 (kk = kend - k0)
-    template <int J0, int J1>
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* region, int q, int64_t k0,
-                                          int64_t kend) const {
-        const int kk = (int)((kend - k0) < 0x7fffffff ? (kend - k0) : 0x7fffffff);
-        const uint32_t kstep = OC ? (uint32_t)k0 * ld2 : (uint32_t)k0 * 2u;
-        // recomputed at every issue (not hoisted out of the main loop)
-        int ln = lane;
-        uint32_t b0 = base;
-        int rm = rem;
-        asm volatile("" : "+v"(ln), "+v"(b0), "+v"(rm));
-#pragma unroll
-        for (int j = J0; j < J1; ++j) {
-            const int g = q * 8 + j;
-            const int lane = ln;
-            const uint32_t base = b0;
-            const int rem = rm;
-            uint32_t off;
-            if (!OC) {
-                const int c = (lane & 7) ^ (((lane >> 3) ^ g) & 7);
-                const bool ok = rem > 8 * g && 8 * c < kk;
-                off = ok ? base + (uint32_t)(8 * g) * ld2 + kstep + (uint32_t)(16 * c) : kOOB;
-            } else {
-                const int k = 2 * g + (lane >> 5);
-                const int c = (lane & 31) ^ ((k & 3) << 2);
-                const bool ok = k < kk && 8 * c < rem;
-                off = ok ? base + (uint32_t)(2 * g) * ld2 + kstep + (uint32_t)(16 * c) : kOOB;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + g * 1024), 16, off, 0, 0, 0);
-        }
-    }
-};
-
-// MFMA operand of a 32-row block from a 64-value stage. For the reduction-
-// contiguous tile, `sw` is this lane's (lane & 7) ^ ((lane >> 3) & 3), the
-// lane-dependent part of the swizzle of rows r0 .. r0+31 (r0 a multiple of 32).
-template <bool OC>
-__device__ __forceinline__ bf16x8 fragment64(const char* region, int r0, int ks, int lane, int sw) {
-    if constexpr (!OC) {
-        const int i = r0 + (lane & 31);
-        const int c = (ks * 2 + (lane >> 5)) ^ sw ^ ((r0 >> 3) & 4);
-        return *reinterpret_cast<const bf16x8*>(region + i * 128 + (c << 4));
-    } else {
-        return fragment<256, true>(region, r0, ks, lane);
-    }
-}
-
-template <bool A_OC, bool B_OC, bool OUT_F32>
-__global__ __launch_bounds__(512) void gemm_pp64_kernel(GemmArgs g) {
-    constexpr int BM = 256, BN = 256;
-    constexpr int TM = 2, TN = 4;  // 64 x 128 wave tile
-    constexpr int BKP = 64, KS = 4;
-    constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
-    constexpr int kStageBytes = kABytes + kBBytes;  // 64 KB
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;
-    const int q = wave & 3;
-    const int wm0 = grp * 128 + (q >> 1) * 64;
-    const int wn0 = (q & 1) * 128;
-
-    const int nbm = (int)((g.M + BM - 1) / BM);
-    const int nbn = (int)((g.N + BN - 1) / BN);
-    const int tiles = nbm * nbn;
-    const int total = gridDim.x;
-    const int lin = blockIdx.x;
-    const int qq = total / kXcds, rem = total % kXcds;
-    const int xcd = lin % kXcds, loc = lin / kXcds;
-    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
-    const int slice = id / tiles;
-    const int pid = id - slice * tiles;
-    const int per_group = kGroupM * nbn;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
-
-    const int64_t kbeg = (int64_t)slice * g.k_split;
-    const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
-    const int nkt = kend > kbeg ? (int)((kend - kbeg + BKP - 1) / BKP) : 0;
-
-    const bool loadA = grp == 0;
-    const int64_t rows_st = loadA ? (A_OC ? g.K : g.M) : (B_OC ? g.K : g.N);
-    const int64_t ld = loadA ? g.lda : g.ldb;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(loadA ? g.A : g.B), 0, (int)(rows_st * ld * 2), kRsrcWord3);
-    Dma64<A_OC> da;
-    Dma64<B_OC> db;
-    if (loadA)
-        da.init(lane, g.lda, m0, g.M);
-    else
-        db.init(lane, g.ldb, n0, g.N);
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    if (nkt > 0) {
-        // stage 0: A from group 0, B from group 1
-        if (loadA)
-            da.template issue<0, 8>(rs, smem, q, kbeg, kend);
-        else
-            db.template issue<0, 8>(rs, smem + kABytes, q, kbeg, kend);
-        waitcnt<0, 0>();
-        __builtin_amdgcn_s_barrier();
-        if (!loadA) {
-            // group 1's idle phase 0: request the B half of stage 1
-            db.template issue<0, 8>(rs, smem + kStageBytes + kABytes, q, kbeg + BKP, kend);
-            waitcnt<8, 0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        bf16x8 fa[KS][TM], fb[KS][TN];
-        for (int t = 0; t < nkt; ++t) {
-            const char* st = smem + (t & 1) * kStageBytes;
-            char* nx = smem + ((t + 1) & 1) * kStageBytes;
-            const int64_t k1 = kbeg + (int64_t)(t + 1) * BKP;
-            // recomputed each stage (not hoisted: keeps 24 addresses out of the register file)
-            int sw = (lane & 7) ^ ((lane >> 3) & 3);
-            asm volatile("" : "+v"(sw));
-            // ---- M(t): fragments of stage t (+ group 0: A half of stage t + 1)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) fa[ks][i] = fragment64<A_OC>(st, wm0 + i * 32, ks, lane, sw);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) fb[ks][j] = fragment64<B_OC>(st + kABytes, wn0 + j * 32, ks, lane, sw);
-            }
-            if (loadA) da.template issue<0, 8>(rs, nx, q, k1, kend);
-            // group 0 ends an even phase here (8 loads may fly); group 1 an odd one
-            if (loadA)
-                waitcnt<8, 0>();
-            else
-                waitcnt<0, 0>();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- C(t) (+ group 1: B half of stage t + 2, spread between MFMA steps)
-            const int64_t k2 = kbeg + (int64_t)(t + 2) * BKP;
-#define FCP64_STEP(KSI)                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j)        \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[KSI][j], fa[KSI][i], acc[i][j], 0, 0, 0); \
-    __builtin_amdgcn_sched_barrier(0);                                                                   \
-    if (!loadA) db.template issue<2 * (KSI), 2 * (KSI) + 2>(rs, (char*)st + kABytes, q, k2, kend);      \
-    __builtin_amdgcn_sched_barrier(0);
-            FCP64_STEP(0)
-            FCP64_STEP(1)
-            FCP64_STEP(2)
-            FCP64_STEP(3)
-#undef FCP64_STEP
-            if (loadA)
-                waitcnt<0, 0>();
-            else
-                waitcnt<8, 0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        if (loadA) {  // matching trailing phase
-            waitcnt<0, 0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        waitcnt<0, 0>();
-    }
-
-    const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm0 + i * 32 + lr;
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int64_t n = n0 + wn0 + j * 32 + gq * 8 + lk * 4;
-                if (n >= g.N) continue;
-                const float v0 = acc[i][j][gq * 4 + 0], v1 = acc[i][j][gq * 4 + 1];
-                const float v2 = acc[i][j][gq * 4 + 2], v3 = acc[i][j][gq * 4 + 3];
-                if (OUT_F32) {
-                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
-                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
-                } else {
-                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
-                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                }
-            }
-        }
-    }
-}
-
 using KernelFn = void (*)(GemmArgs);
 struct Entry {
     KernelFn fn;
@@ -967,25 +722,14 @@ const Entry kPipe[kNumTiles * 8] = {
     FCP_TILE(128, 128),
 };
 
-#define FCPP_K(AOC, BOC, F32, KS, MF)                                                              \
-    Entry {                                                                                        \
-        gemm_pp_kernel<AOC, BOC, F32, KS, MF>,                                                     \
-            "gemm_pp_kernel<" #AOC ", " #BOC ", " #F32 ", " #KS ", " #MF ">"                       \
-    }
-#define FCPP_ALL(KS, MF)                                                                                        \
-    FCPP_K(false, false, false, KS, MF), FCPP_K(false, true, false, KS, MF), FCPP_K(true, false, false, KS, MF), \
-        FCPP_K(true, true, false, KS, MF), FCPP_K(false, false, true, KS, MF), FCPP_K(false, true, true, KS, MF), \
-        FCPP_K(true, false, true, KS, MF), FCPP_K(true, true, true, KS, MF)
-// [variant: 48-value stages, 32-value stages, 32-value stages with 16x16x32 MFMA][out_f32][a_oc][b_oc]
-const Entry kPingPong[3][8] = {{FCPP_ALL(3, 32)}, {FCPP_ALL(2, 32)}, {FCPP_ALL(2, 16)}};
-
-#define FCPP64_K(AOC, BOC, F32) \
-    Entry { gemm_pp64_kernel<AOC, BOC, F32>, "gemm_pp64_kernel<" #AOC ", " #BOC ", " #F32 ">" }
-const Entry kPingPong64[8] = {
-    FCPP64_K(false, false, false), FCPP64_K(false, true, false), FCPP64_K(true, false, false),
-    FCPP64_K(true, true, false),   FCPP64_K(false, false, true), FCPP64_K(false, true, true),
-    FCPP64_K(true, false, true),   FCPP64_K(true, true, true),
-};
+#define FCPP_K(AOC, BOC, F32, MF) \
+    Entry { gemm_pp_kernel<AOC, BOC, F32, MF>, "gemm_pp_kernel<" #AOC ", " #BOC ", " #F32 ", " #MF ">" }
+#define FCPP_ALL(MF)                                                                                    \
+    FCPP_K(false, false, false, MF), FCPP_K(false, true, false, MF), FCPP_K(true, false, false, MF),    \
+        FCPP_K(true, true, false, MF), FCPP_K(false, false, true, MF), FCPP_K(false, true, true, MF),   \
+        FCPP_K(true, false, true, MF), FCPP_K(true, true, true, MF)
+// [MFMA: 32x32x16, 16x16x32][out_f32][a_oc][b_oc]
+const Entry kPingPong[2][8] = {{FCPP_ALL(32)}, {FCPP_ALL(16)}};
 
 #define FCPP1B_K(AOC, BOC, F32, MF) \
     Entry { gemm_pp1b_kernel<AOC, BOC, F32, MF>, "gemm_pp1b_kernel<" #AOC ", " #BOC ", " #F32 ", " #MF ">" }
@@ -1005,28 +749,23 @@ const char* pipe_kernel_name(int tile, bool a_oc, bool b_oc, bool out_f32) {
     return pipe_entry(tile, a_oc, b_oc, out_f32).name;
 }
 
-const Entry& pingpong_entry(int depth, bool a_oc, bool b_oc, bool out_f32) {
+const Entry& pingpong_entry(int variant, bool a_oc, bool b_oc, bool out_f32) {
     const int i = (out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0);
-    switch (depth) {
-        case 0: return kPingPong[0][i];
-        case 1: return kPingPong[1][i];
-        case 2: return kPingPong64[i];
-        case 3: return kPingPong1b[0][i];
-        case 4: return kPingPong[2][i];
-        default: return kPingPong1b[1][i];
-    }
+    // variant bit 0: one barrier per stage; bit 1: 16x16x32 MFMAs
+    const int mf = (variant >> 1) & 1;
+    return (variant & 1) ? kPingPong1b[mf][i] : kPingPong[mf][i];
 }
 
-const char* pingpong_kernel_name(int depth, bool a_oc, bool b_oc, bool out_f32) {
-    return pingpong_entry(depth, a_oc, b_oc, out_f32).name;
+const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32) {
+    return pingpong_entry(variant, a_oc, b_oc, out_f32).name;
 }
 
-hipError_t launch_gemm_pingpong(int depth, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+hipError_t launch_gemm_pingpong(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                                 hipStream_t stream) {
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + 255) / 256) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pingpong_entry(depth, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks),
+    hipLaunchKernelGGL(pingpong_entry(variant, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks),
                        dim3(512), 0, stream, args);
     return hipGetLastError();
 }
