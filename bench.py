@@ -35,7 +35,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "sharded_fc_layer_amd", "csrc", f)
-                  for f in ("gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip")]
+                  for f in ("gemm_common.h", "gemm_pipe.hip", "gemm_w4.hip", "gemm_bf16.hip", "aux_kernels.hip",
+                            "fcshard_api.hip")]
 
 
 def kernel_source_hash() -> str:

@@ -6,6 +6,7 @@ shared library next to this file.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -18,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfcshard.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip"]
+SOURCES = ["gemm_pipe.hip", "gemm_w4.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip"]
 
 # packed-fp32 instructions are switched off for all device code
 HIPCC_FLAGS = [
@@ -58,6 +59,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    try:  # every symbol must resolve (a kernel instance without a host stub would not)
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"the linked library does not load: {e}") from None
     os.replace(tmp, LIB)
     return LIB
 

@@ -27,7 +27,7 @@
 #include <tuple>
 #include <vector>
 
-#include "../../include/fcshard.h"
+#include "fcshard.h"
 #include "fcshard_internal.h"
 
 namespace fcs {
@@ -37,8 +37,11 @@ constexpr int kSplits[] = {1, 2, 4};
 constexpr int kNumSplits = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // 0: 4-wave pipelined, 1: simple, 2-5: 8-wave ping-pong (256 x 256), variant
-// = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs
-constexpr int kNumFamilies = 6;
+// = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
+// 6, 7: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), a
+// barrier every stage (6) or every second stage (7)
+constexpr int kNumFamilies = 8;
+constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
 constexpr int kMaxDevices = 64;
@@ -47,7 +50,7 @@ struct Plan {
     int tile;
     int split;   // number of reduction slices requested
     int copy;    // bit mask
-    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2)
+    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-7 one wave per SIMD
 };
 
 Plan decode_plan(int id) {
@@ -127,6 +130,7 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
     if (pl.family >= 2 && pl.tile != 0) return false;
+    if (pl.family >= kFamilyW4 && p.K % 64 != 0) return false;  // stages run in pairs, no odd tail
     if (pl.family != 1) {
         const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * p.K * 2);
         const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * p.K * 2);
@@ -254,8 +258,9 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
         float* part = reinterpret_cast<float*>(base + w.p_off);
         g.C = part;
         g.c_split_stride = p.M * p.N;
-        e = pl.family == 0   ? launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, true, g, s)
-            : pl.family >= 2 ? launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, true, g, s)
+        e = pl.family == 0            ? launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, true, g, s)
+            : pl.family >= kFamilyW4  ? launch_gemm_w4(pl.family - kFamilyW4, p.a_oc, p.b_oc, true, g, s)
+            : pl.family >= 2          ? launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, true, g, s)
                              : launch_gemm(pl.tile, p.a_oc, p.b_oc, true, aligned, g, s);
         if (e != hipSuccess) return e;
         return launch_splitk_reduce(part, p.C, p.out_f32, p.M * p.N, slices, p.M * p.N, s);
@@ -263,6 +268,7 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
     g.C = p.C;
     g.c_split_stride = 0;
     if (pl.family == 0) return launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, p.out_f32, g, s);
+    if (pl.family >= kFamilyW4) return launch_gemm_w4(pl.family - kFamilyW4, p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= 2) return launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, p.out_f32, g, s);
     return launch_gemm(pl.tile, p.a_oc, p.b_oc, p.out_f32, aligned, g, s);
 }
@@ -378,8 +384,9 @@ std::string describe(const Problem& p, int id, int64_t ws_have) {
                          (uintptr_t)p.C % 16 == 0 && (q.A == nullptr || (uintptr_t)q.A % 16 == 0) &&
                          (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
     const bool f32 = slices > 1 ? true : p.out_f32;
-    const char* kname = pl.family == 0   ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
-                        : pl.family >= 2 ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
+    const char* kname = pl.family == 0            ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
+                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, q.a_oc, q.b_oc, f32)
+                        : pl.family >= 2          ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
                                          : gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc, f32,
                                                             aligned);
     char buf[512];

@@ -57,6 +57,14 @@ hipError_t launch_gemm_pingpong(int variant, bool a_oc, bool b_oc, bool out_f32,
                                 hipStream_t stream);
 const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
 
+// Enqueue the 4-wave (one wave per SIMD) GEMM, 256 x 256 tile, 128 x 128
+// per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
+// launch_gemm_pipe, and K a multiple of 64). variant 0: a barrier every
+// reduction stage; 1: every second stage.
+hipError_t launch_gemm_w4(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+                          hipStream_t stream);
+const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
+
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                  hipStream_t stream);

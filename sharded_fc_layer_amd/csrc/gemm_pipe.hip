@@ -32,103 +32,11 @@
 //  * Blocks are remapped so that each XCD works through one contiguous range
 //    of tiles, in groups of 8 tile-rows (L2 sharing within an XCD).
 //  * Reduction slices (split-K) write fp32 partials to separate planes.
-#include "fcshard_internal.h"
+#include "gemm_common.h"
 
 namespace fcs {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
-constexpr int kBK = 32;        // reduction values per stage
-constexpr int kStages = 4;     // LDS ring depth
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
-constexpr uint32_t kOOB = 0x80000000u;       // offset past any operand (< 2 GiB)
-constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
-
-__device__ __forceinline__ uint32_t rc_slot(int i, int c) { return i * 64 + ((c ^ ((i >> 2) & 3)) << 4); }
-
-template <int R>
-__device__ __forceinline__ uint32_t oc_slot(int k, int c) {
-    return k * (R * 2) + ((c ^ ((k & 3) << 2)) << 4);
-}
-
-// s_waitcnt with vmcnt = vm, lgkmcnt = lgkm (expcnt not waited)
-template <int VM, int LGKM>
-__device__ __forceinline__ void waitcnt() {
-    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
-}
-
-// One operand tile of R rows (output index) x 32 reduction values per stage.
-template <int R, bool OC>
-struct Dma {
-    static constexpr int kInstr = R / 64;  // 1 KB instructions per wave per stage
-    uint32_t base[kInstr];                 // byte offset at reduction 0, or kOOB
-    int kk[kInstr];                        // reduction offset of the chunk within a stage
-
-    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int64_t row0, int64_t rows) {
-#pragma unroll
-        for (int j = 0; j < kInstr; ++j) {
-            if (!OC) {
-                const int i = (wave * kInstr + j) * 16 + (lane >> 2);
-                const int c = (lane & 3) ^ ((lane >> 4) & 3);
-                kk[j] = 8 * c;
-                base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
-            } else {
-                constexpr int CPR = R / 8;     // 16-byte chunks per reduction row
-                constexpr int RPI = 64 / CPR;  // reduction rows per instruction
-                const int k = (wave * kInstr + j) * RPI + lane / CPR;
-                const int c = (lane % CPR) ^ ((k & 3) << 2);
-                kk[j] = k;
-                base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
-            }
-        }
-    }
-
-    // issue instructions j in [lo, hi) of this wave's share of one stage
-    template <int LO, int HI>
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* region, int64_t k0, int64_t kend,
-                                          int64_t ld, int wave) const {
-        const uint32_t step = OC ? (uint32_t)(k0 * ld * 2) : (uint32_t)(k0 * 2);
-#pragma unroll
-        for (int j = (LO > 0 ? LO : 0); j < (HI < kInstr ? HI : kInstr); ++j) {
-            const uint32_t off = (base[j] == kOOB || k0 + kk[j] >= kend) ? kOOB : base[j] + step;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wave * kInstr + j) * 1024), 16,
-                                                     off, 0, 0, 0);
-        }
-    }
-};
-
-// MFMA operand of one 32-row block (rows r0 .. r0+31), reduction step ks (16 values)
-template <int R, bool OC>
-__device__ __forceinline__ bf16x8 fragment(const char* region, int r0, int ks, int lane) {
-    if (!OC) {
-        const int i = r0 + (lane & 31);
-        const int c = ks * 2 + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
-    } else {
-        const int g = lane >> 4, j = lane & 15;
-        const int col = r0 + 16 * (g & 1) + 4 * (j & 3);
-        const int k = ks * 16 + 8 * (g >> 1) + (j >> 2);
-        const int c = col >> 3, half = (col & 7) << 1;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<R>(k, c) + half));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<R>(k + 4, c) + half));
-        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, v);
-    }
-}
 
 template <int BM, int BN, bool A_OC, bool B_OC, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
@@ -145,24 +53,9 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
     const int wm0 = (wave >> 1) * WTM;
     const int wn0 = (wave & 1) * WTN;
 
-    // ---- block id -> (slice, tile row, tile col)
-    const int nbm = (int)((g.M + BM - 1) / BM);
-    const int nbn = (int)((g.N + BN - 1) / BN);
-    const int tiles = nbm * nbn;
-    const int total = gridDim.x;
-    const int lin = blockIdx.x;
-    const int q = total / kXcds, rem = total % kXcds;
-    const int xcd = lin % kXcds, loc = lin / kXcds;
-    const int id = xcd * q + (xcd < rem ? xcd : rem) + loc;
-    const int slice = id / tiles;
-    const int pid = id - slice * tiles;
-    const int per_group = kGroupM * nbn;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const BlockTile bt = map_block<BM, BN>(g);
+    const int slice = bt.slice;
+    const int64_t m0 = bt.m0, n0 = bt.n0;
 
     const int64_t kbeg = (int64_t)slice * g.k_split;
     const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
@@ -304,137 +197,6 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
 // reads has landed".
 
 
-// loads of one operand tile (256 rows x BKP reduction values) shared by 4 waves
-template <bool OC, int BKP>
-struct DmaPP {
-    static_assert(BKP == 32, "32-value stages");
-    static constexpr int R = 256;
-    static constexpr int kInstr = R * BKP * 2 / 1024 / 4;  // per wave
-    uint32_t base[kInstr];
-    int kk[kInstr];
-
-    __device__ __forceinline__ void init(int wq, int lane, int64_t ld, int64_t row0, int64_t rows) {
-#pragma unroll
-        for (int j = 0; j < kInstr; ++j) {
-            const int p = (wq * kInstr + j) * 64 + lane;  // 16-byte slot in the tile
-            if (!OC) {
-                constexpr int CPR = BKP / 8;
-                const int i = p / CPR, pc = p % CPR;
-                const int c = pc ^ ((i >> 2) & 3);
-                kk[j] = 8 * c;
-                base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
-            } else {
-                constexpr int CPR = R / 8;
-                const int k = p / CPR;
-                const int c = (p % CPR) ^ ((k & 3) << 2);
-                kk[j] = k;
-                base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
-            }
-        }
-    }
-
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char* region, int64_t k0, int64_t kend,
-                                          int64_t ld, int wq) const {
-        const uint32_t step = OC ? (uint32_t)(k0 * ld * 2) : (uint32_t)(k0 * 2);
-#pragma unroll
-        for (int j = 0; j < kInstr; ++j) {
-            const uint32_t off = (base[j] == kOOB || k0 + kk[j] >= kend) ? kOOB : base[j] + step;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wq * kInstr + j) * 1024), 16,
-                                                     off, 0, 0, 0);
-        }
-    }
-};
-
-template <bool OC, int BKP>
-__device__ __forceinline__ bf16x8 fragment_pp(const char* region, int r0, int ks, int lane) {
-    if constexpr (!OC) {
-        const int i = r0 + (lane & 31);
-        const int c = ks * 2 + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
-    } else {
-        return fragment<256, true>(region, r0, ks, lane);
-    }
-}
-
-// accumulator type and MFMA of one output block: 32 x 32 x 16 or 16 x 16 x 32
-template <int MF>
-struct AccT;
-template <>
-struct AccT<32> {
-    typedef f32x16 type;
-    static constexpr int n = 16;
-};
-template <>
-struct AccT<16> {
-    typedef f32x4 type;
-    static constexpr int n = 4;
-};
-
-template <int MF>
-__device__ __forceinline__ typename AccT<MF>::type mfma_bf16(bf16x8 a, bf16x8 b, typename AccT<MF>::type c) {
-    if constexpr (MF == 32)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// MFMA operand of an MF-row block at r0, reduction step ks of a BKP-value stage.
-// 16 x 16 x 32: lane l holds block row l % 16 and reduction values
-// 32 ks + 8 (l / 16) .. +7; for output-contiguous tiles the 16-lane group g
-// reads rows 32 ks + 8 g (+4) with two ds_read_b64_tr_b16.
-template <bool OC, int BKP, int MF>
-__device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks, int lane) {
-    if constexpr (MF == 32) {
-        return fragment_pp<OC, BKP>(region, r0, ks, lane);
-    } else if constexpr (!OC) {
-        const int i = r0 + (lane & 15);
-        const int c = ks * 4 + (lane >> 4);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
-    } else {
-        const int g = lane >> 4, j = lane & 15;
-        const int col = r0 + 4 * (j & 3);
-        const int k = ks * 32 + 8 * g + (j >> 2);
-        const int c = col >> 3, half = (col & 7) << 1;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<256>(k, c) + half));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<256>(k + 4, c) + half));
-        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, v);
-    }
-}
-
-// epilogue of one wave tile: rows m0 + wm0 .., columns n0 + wn0 ..; each lane
-// holds 4 consecutive output columns of one row per block
-template <int MF, int TM, int TN, bool OUT_F32>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t m0, int64_t n0, int wm0, int wn0,
-                                           int lane, const typename AccT<MF>::type (&acc)[TM][TN]) {
-    constexpr int GR = MF == 32 ? 4 : 1;  // 4-column groups per lane per block
-    const int lr = lane & (MF - 1), lk = MF == 32 ? (lane >> 5) : (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm0 + i * MF + lr;
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int gq = 0; gq < GR; ++gq) {
-                const int64_t n = n0 + wn0 + j * MF + gq * 8 + lk * 4;
-                if (n >= g.N) continue;
-                const float v0 = acc[i][j][gq * 4 + 0], v1 = acc[i][j][gq * 4 + 1];
-                const float v2 = acc[i][j][gq * 4 + 2], v3 = acc[i][j][gq * 4 + 3];
-                if (OUT_F32) {
-                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
-                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
-                } else {
-                    __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
-                    *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                }
-            }
-        }
-    }
-}
-
 template <bool A_OC, bool B_OC, bool OUT_F32, int MF>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256;
@@ -457,23 +219,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     const int wm0 = grp * 128 + (q >> 1) * 64;
     const int wn0 = (q & 1) * 128;
 
-    const int nbm = (int)((g.M + BM - 1) / BM);
-    const int nbn = (int)((g.N + BN - 1) / BN);
-    const int tiles = nbm * nbn;
-    const int total = gridDim.x;
-    const int lin = blockIdx.x;
-    const int qq = total / kXcds, rem = total % kXcds;
-    const int xcd = lin % kXcds, loc = lin / kXcds;
-    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
-    const int slice = id / tiles;
-    const int pid = id - slice * tiles;
-    const int per_group = kGroupM * nbn;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const BlockTile bt = map_block<BM, BN>(g);
+    const int slice = bt.slice;
+    const int64_t m0 = bt.m0, n0 = bt.n0;
 
     const int64_t kbeg = (int64_t)slice * g.k_split;
     const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
@@ -590,23 +338,9 @@ __global__ __launch_bounds__(512) void gemm_pp1b_kernel(GemmArgs g) {
     const int wm0 = grp * 128 + (q >> 1) * 64;
     const int wn0 = (q & 1) * 128;
 
-    const int nbm = (int)((g.M + BM - 1) / BM);
-    const int nbn = (int)((g.N + BN - 1) / BN);
-    const int tiles = nbm * nbn;
-    const int total = gridDim.x;
-    const int lin = blockIdx.x;
-    const int qq = total / kXcds, rem = total % kXcds;
-    const int xcd = lin % kXcds, loc = lin / kXcds;
-    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
-    const int slice = id / tiles;
-    const int pid = id - slice * tiles;
-    const int per_group = kGroupM * nbn;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const BlockTile bt = map_block<BM, BN>(g);
+    const int slice = bt.slice;
+    const int64_t m0 = bt.m0, n0 = bt.n0;
 
     const int64_t kbeg = (int64_t)slice * g.k_split;
     const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;

@@ -138,7 +138,10 @@ def test_exact_power_of_two_scaled_inputs():
             assert_exact(host(c.gpu(op, dt)), O, dt, f"{op} pow2 dtype={dt}")
 
 
-@pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17)],
+# (320, 576, 192): every reduction length (576, 192, 320) is a multiple of 64,
+# so the kernels that take reduction stages in pairs run too, with ragged
+# output tiles and two- and four-way reduction splits.
+@pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
