@@ -38,8 +38,8 @@ constexpr int kNumSplits = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // 0: 4-wave pipelined, 1: simple, 2-5: 8-wave ping-pong (256 x 256), variant
 // = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
-// 6, 7: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), a
-// barrier every stage (6) or every second stage (7)
+// 6, 7: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
+// 32-value (6) or 64-value (7) reduction stages
 constexpr int kNumFamilies = 8;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
@@ -130,7 +130,13 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
     if (pl.family >= 2 && pl.tile != 0) return false;
-    if (pl.family >= kFamilyW4 && p.K % 64 != 0) return false;  // stages run in pairs, no odd tail
+    if (pl.family >= kFamilyW4) {  // stages run in pairs, no odd tail: every slice a multiple of 64 or 128
+        const int64_t q = pl.family == kFamilyW4 ? 64 : 128;
+        int64_t ks;
+        int slices;
+        split_geometry(p.K, pl.split, &ks, &slices);
+        if (p.K % q != 0 || (slices > 1 && ks % q != 0)) return false;
+    }
     if (pl.family != 1) {
         const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * p.K * 2);
         const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * p.K * 2);

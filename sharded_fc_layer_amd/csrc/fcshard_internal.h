@@ -59,8 +59,9 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 
 // Enqueue the 4-wave (one wave per SIMD) GEMM, 256 x 256 tile, 128 x 128
 // per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
-// launch_gemm_pipe, and K a multiple of 64). variant 0: a barrier every
-// reduction stage; 1: every second stage.
+// launch_gemm_pipe, and K a multiple of 64, of 128 for variant 1).
+// variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
+// 2 slots (whole-cache-line rows for reduction-contiguous operands).
 hipError_t launch_gemm_w4(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream);
 const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);

@@ -28,6 +28,20 @@ constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
 
 __device__ __forceinline__ uint32_t rc_slot(int i, int c) { return i * 64 + ((c ^ ((i >> 2) & 3)) << 4); }
 
+// Reduction-contiguous tile row of BKP values: 16-byte chunk c of row i.
+// 32 values (64 B rows): chunk ^ ((i >> 2) & 3). 64 values (128 B rows, one
+// cache line): chunk ^ ((i >> 1) & 7), so the 16 rows one 16-lane group of a
+// 16x16x32 operand read touches fall on 16 different 16-byte bank groups.
+template <int BKP>
+__device__ __forceinline__ int rc_swizzle(int i) {
+    static_assert(BKP == 32 || BKP == 64, "32- or 64-value rows");
+    return BKP == 32 ? ((i >> 2) & 3) : ((i >> 1) & 7);
+}
+template <int BKP>
+__device__ __forceinline__ uint32_t rc_slot_k(int i, int c) {
+    return i * (BKP * 2) + ((c ^ rc_swizzle<BKP>(i)) << 4);
+}
+
 template <int R>
 __device__ __forceinline__ uint32_t oc_slot(int k, int c) {
     return k * (R * 2) + ((c ^ ((k & 3) << 2)) << 4);
@@ -104,7 +118,7 @@ __device__ __forceinline__ bf16x8 fragment(const char* region, int r0, int ks, i
 // loads of one operand tile (256 rows x BKP reduction values) shared by 4 waves
 template <bool OC, int BKP>
 struct DmaPP {
-    static_assert(BKP == 32, "32-value stages");
+    static_assert(BKP == 32 || BKP == 64, "32- or 64-value stages");
     static constexpr int R = 256;
     static constexpr int kInstr = R * BKP * 2 / 1024 / 4;  // per wave
     uint32_t base[kInstr];
@@ -117,7 +131,7 @@ struct DmaPP {
             if (!OC) {
                 constexpr int CPR = BKP / 8;
                 const int i = p / CPR, pc = p % CPR;
-                const int c = pc ^ ((i >> 2) & 3);
+                const int c = pc ^ rc_swizzle<BKP>(i);
                 kk[j] = 8 * c;
                 base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
             } else {
@@ -139,6 +153,13 @@ struct DmaPP {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wq * kInstr + j) * 1024), 16,
                                                      off, 0, 0, 0);
         }
+    }
+
+    // Load instruction j alone of issue_full (for hand-interleaved schedules).
+    __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rsrc, char* region, uint32_t step, int wq,
+                                              int j) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wq * kInstr + j) * 1024), 16,
+                                                 base[j] + step, 0, 0, 0);
     }
 
     // Same loads for a stage that lies wholly inside the reduction range (no
@@ -198,7 +219,7 @@ __device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks
     } else if constexpr (!OC) {
         const int i = r0 + (lane & 15);
         const int c = ks * 4 + (lane >> 4);
-        return *reinterpret_cast<const bf16x8*>(region + rc_slot(i, c));
+        return *reinterpret_cast<const bf16x8*>(region + rc_slot_k<BKP>(i, c));
     } else {
         const int g = lane >> 4, j = lane & 15;
         const int col = r0 + 4 * (j & 3);

@@ -1,43 +1,45 @@
-// 4-wave bf16 GEMM for gfx950 (MI355X), one wave per SIMD: the local
+// 4-wave bf16 GEMMs for gfx950 (MI355X), one wave per SIMD: the local
 // products of one GPU's FC-layer shard under the 3D parallel matrix multiply
 // (sciencestack.ai/paper/2502.08145, Figure 1), bf16 in with fp32
 // accumulation (mlsanity.com/paper/2502.08145, Abstract: bf16 training).
 //
 // Requirements (checked by the caller): M, N multiples of 8, K and the
-// split-K slice length multiples of 64, 16-byte aligned operands and output,
-// every operand smaller than 2 GiB.
+// split-K slice length multiples of 64 (128 for the 64-value-stage kernel),
+// 16-byte aligned operands and output, every operand smaller than 2 GiB.
 //
-// Structure (256 threads = 4 wave64s in a 2 x 2 grid, 256 x 256 block tile):
+// Common structure (256 threads = 4 wave64s in a 2 x 2 grid, 256 x 256 tile):
 //  * Each wave owns a 128 x 128 output tile: 8 x 8 blocks of
 //    v_mfma_f32_16x16x32_bf16, 256 fp32 accumulators per lane. With one wave
 //    per SIMD a wave has the SIMD's whole register file, so its tile is four
 //    times that of an 8-wave kernel's wave, and each byte read from LDS feeds
 //    twice the MFMA work (A and B fragments are each shared by 8 MFMAs).
-//  * Reduction stages of 32 values in a ring of S = 4 LDS slots (128 KB),
-//    filled by direct-to-LDS buffer loads issued S stages ahead; layouts and
+//  * Operands reach LDS through direct-to-LDS buffer loads; layouts and
 //    swizzles are those of gemm_common.h.
-//  * Stage t: the wave issues the LDS reads of stage t + 1 into the second
-//    fragment register set while it runs the 64 MFMAs of stage t from the
-//    first. Scheduling groups put one LDS read after each of the first MFMAs
-//    and then spread the stage's loads evenly over the remaining MFMAs: a
-//    burst of loads would fill the address unit's queue, and a wave stalled
-//    on a load issue leaves its SIMD's MFMA pipe idle (one wave per SIMD).
-//  * Barriers (template argument P): with P = 1 every stage opens with one.
-//    Each wave first waits for its own loads of stage t + 1 and its LDS reads
-//    of stage t (already in registers), then the barrier; after it the wave
-//    issues the loads of stage t + S into stage t's slot, which every wave
-//    has finished reading. With P = 2 only even stages open with a barrier:
-//    it certifies stages t + 1 and t + 2 (the next two stages' LDS reads)
-//    and frees the slots of stages t - 1 and t for the loads of t + 3 and
-//    t + 4, which then have two stages of MFMA work to land. Half the
-//    barriers, the same ring.
-//  * The stage loop is unrolled twice (the two fragment register sets) with
-//    no odd tail, so the reduction of every slice must be a multiple of 64.
-//  * Every stage issues the same number of loads (the prefetches past the end
-//    of the reduction reload its last stage into slots nobody reads), so "at
-//    most two stages of loads in flight" is exactly "stage t + 1 has landed".
-//    Output rows and columns past the matrix keep an out-of-range offset and
-//    read zeros.
+//  * Two fragment register sets: the wave issues the LDS reads of the next
+//    32-value reduction step into one set while it runs the 64 MFMAs of the
+//    current step from the other. Scheduling groups put one LDS read after
+//    each of the first MFMAs and then spread the loads evenly over the
+//    remaining MFMAs: a burst of loads would fill the address unit's queue,
+//    and a wave stalled on a load issue leaves its SIMD's MFMA pipe idle.
+//  * Stages past the end of the reduction (prefetches nobody reads) reload
+//    the last stage, so every load stays inside its operand and each stage
+//    issues the same number of loads; output rows and columns past the
+//    matrix keep an out-of-range offset and read zeros.
+//
+// gemm_w4_kernel: stages of 32 values in a ring of 4 slots (128 KB). Each
+// stage opens with a barrier: every wave first waits for its own loads of
+// stage t + 1 and its LDS reads of stage t (already in registers); after the
+// barrier it issues the loads of stage t + 4 into stage t's slot, which every
+// wave has finished reading. Loads have three stages of MFMA work to land.
+//
+// gemm_w4k64_kernel: stages of 64 values (reduction-contiguous tile rows are
+// then one whole 128-byte cache line; with 64-byte rows every line is fetched
+// from L2 twice) in two slots of 64 KB; each operand tile of each slot is its
+// own __shared__ array so that the compiler can tell the loads into one from
+// the reads of another (and waits only where a read needs them). A stage
+// is two 32-value steps; the barrier sits before the second: it certifies
+// stage t + 1 (whose first step the wave reads next) and frees stage t's
+// slot for the loads of stage t + 2, which have two steps to land.
 #include "gemm_common.h"
 
 namespace fcs {
@@ -46,146 +48,256 @@ namespace {
 
 constexpr int kW4Threads = 256;
 
-template <bool A_OC, bool B_OC, bool OUT_F32, int P>
-__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
-    GemmArgs g) {
-    static_assert(P == 1 || P == 2, "a barrier every stage or every second stage");
-    constexpr int BM = 256, BN = 256, MF = 16;
-    constexpr int TM = 8, TN = 8;  // 16 x 16 blocks per wave tile
-    constexpr int BKP = 32, S = 4;
-    constexpr int kABytes = BM * BKP * 2, kBBytes = BN * BKP * 2;
-    constexpr int kStageBytes = kABytes + kBBytes;
-    constexpr int kLoads = DmaPP<A_OC, BKP>::kInstr + DmaPP<B_OC, BKP>::kInstr;  // per wave per stage
-    // P = 1: the barrier before stage t lets stage t + 1 be read and frees
-    // stage t's slot for stage t + S (two stages of loads stay in flight).
-    // P = 2: the barrier before an even stage t lets stages t + 1 and t + 2
-    // be read and frees the slots of t - 1 and t for stages t + 3 and t + 4,
-    // which have the two stages up to the next barrier to land.
-    constexpr int kInFlight = P == 1 ? (S - 2) * kLoads : 0;
-    constexpr int kReads = (A_OC ? 2 : 1) * TM + (B_OC ? 2 : 1) * TN;  // LDS read instructions per stage
-    __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
+// block set-up shared by both kernels
+struct W4Setup {
+    int lane, wave, wm0, wn0, slice, nkt;
+    int64_t m0, n0, kbeg, kend;
+    __amdgpu_buffer_rsrc_t ra, rb;
+};
 
+template <bool A_OC, bool B_OC, int BKP>
+__device__ __forceinline__ W4Setup w4_setup(const GemmArgs& g) {
+    W4Setup w;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave >> 1) * 128;
-    const int wn0 = (wave & 1) * 128;
-
-    const BlockTile bt = map_block<BM, BN>(g);
-    const int slice = bt.slice;
-    const int64_t m0 = bt.m0, n0 = bt.n0;
-
-    const int64_t kbeg = (int64_t)slice * g.k_split;
-    const int64_t kend = (kbeg + g.k_split < g.K) ? kbeg + g.k_split : g.K;
-    const int nkt = kend > kbeg ? (int)((kend - kbeg + BKP - 1) / BKP) : 0;
-
+    w.lane = tid & 63;
+    w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    w.wm0 = (w.wave >> 1) * 128;
+    w.wn0 = (w.wave & 1) * 128;
+    const BlockTile bt = map_block<256, 256>(g);
+    w.slice = bt.slice;
+    w.m0 = bt.m0;
+    w.n0 = bt.n0;
+    w.kbeg = (int64_t)w.slice * g.k_split;
+    w.kend = (w.kbeg + g.k_split < g.K) ? w.kbeg + g.k_split : g.K;
+    w.nkt = w.kend > w.kbeg ? (int)((w.kend - w.kbeg + BKP - 1) / BKP) : 0;
     const int64_t a_rows = A_OC ? g.K : g.M;  // storage rows of each operand
     const int64_t b_rows = B_OC ? g.K : g.N;
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, (int)(a_rows * g.lda * 2), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.B, 0, (int)(b_rows * g.ldb * 2), kRsrcWord3);
+    w.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, (int)(a_rows * g.lda * 2), kRsrcWord3);
+    w.rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, 0, (int)(b_rows * g.ldb * 2), kRsrcWord3);
+    return w;
+}
+
+// scheduling groups of one 64-MFMA step: one LDS read after each of the
+// first READS MFMAs, then LOADS loads spread evenly over the rest
+template <int READS, int LOADS>
+__device__ __forceinline__ void w4_interleave() {
+    constexpr int kGap = LOADS > 0 ? (64 - READS) / LOADS : 1;
+    static_assert(LOADS == 0 || kGap >= 1, "too many loads for one step");
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (u < READS)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        else if ((u - READS) % kGap == 0 && (u - READS) / kGap < LOADS)
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one load
+    }
+}
+
+#define FCW4_MFMA_STEP(SET)                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) _Pragma("unroll") for (int j = 0; j < 8; ++j)      \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, 0);
+
+template <bool A_OC, bool B_OC, bool OUT_F32>
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
+    GemmArgs g) {
+    constexpr int MF = 16, BKP = 32, S = 4;
+    constexpr int kABytes = 256 * BKP * 2;
+    constexpr int kStageBytes = 2 * kABytes;
+    constexpr int kLoads = DmaPP<A_OC, BKP>::kInstr + DmaPP<B_OC, BKP>::kInstr;  // per wave per stage
+    constexpr int kInFlight = (S - 2) * kLoads;
+    constexpr int kReads = (A_OC ? 16 : 8) + (B_OC ? 16 : 8);  // LDS read instructions per step
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStageBytes];
+
+    const W4Setup w = w4_setup<A_OC, B_OC, BKP>(g);
+    const int lane = w.lane, wave = w.wave, wm0 = w.wm0, wn0 = w.wn0, nkt = w.nkt;
     DmaPP<A_OC, BKP> da;
     DmaPP<B_OC, BKP> db;
-    da.init(wave, lane, g.lda, m0, g.M);
-    db.init(wave, lane, g.ldb, n0, g.N);
+    da.init(wave, lane, g.lda, w.m0, g.M);
+    db.init(wave, lane, g.ldb, w.n0, g.N);
 
-    f32x4 acc[TM][TN];
+    f32x4 acc[8][8];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 fa[2][8], fb[2][8];
 
-    bf16x8 fa[2][TM], fb[2][TN];
-
-    // Stage SIDX into its ring slot. Stages past the end (the last S - 1
-    // prefetches, never read) reload the last stage instead, so every load
-    // stays inside its operand and no reduction check is needed.
-#define FCW4_ISSUE(SIDX)                                                                  \
-    {                                                                                     \
-        char* st_ = smem + ((SIDX) % S) * kStageBytes;                                    \
-        const int64_t k0_ = kbeg + (int64_t)((SIDX) < nkt ? (SIDX) : nkt - 1) * BKP;      \
-        da.issue_full(ra, st_, (uint32_t)(A_OC ? k0_ * g.lda * 2 : k0_ * 2), wave);       \
-        db.issue_full(rb, st_ + kABytes, (uint32_t)(B_OC ? k0_ * g.ldb * 2 : k0_ * 2), wave); \
+#define FCW4_ISSUE(SIDX)                                                                          \
+    {                                                                                             \
+        char* st_ = smem + ((SIDX) % S) * kStageBytes;                                            \
+        const int64_t k0_ = w.kbeg + (int64_t)((SIDX) < nkt ? (SIDX) : nkt - 1) * BKP;            \
+        da.issue_full(w.ra, st_, (uint32_t)(A_OC ? k0_ * g.lda * 2 : k0_ * 2), wave);             \
+        db.issue_full(w.rb, st_ + kABytes, (uint32_t)(B_OC ? k0_ * g.ldb * 2 : k0_ * 2), wave);   \
     }
-#define FCW4_READ(T, BUF)                                                                                    \
-    {                                                                                                        \
-        const char* st_ = smem + ((T) % S) * kStageBytes;                                                    \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[BUF][i] =                                          \
-            fragment_mf<A_OC, BKP, MF>(st_, wm0 + i * MF, 0, lane);                                          \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[BUF][j] =                                          \
-            fragment_mf<B_OC, BKP, MF>(st_ + kABytes, wn0 + j * MF, 0, lane);                                \
+#define FCW4_READ(T, SET)                                                                                 \
+    {                                                                                                     \
+        const char* st_ = smem + ((T) % S) * kStageBytes;                                                 \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) fa[SET][i] =                                        \
+            fragment_mf<A_OC, BKP, MF>(st_, wm0 + i * MF, 0, lane);                                       \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) fb[SET][j] =                                        \
+            fragment_mf<B_OC, BKP, MF>(st_ + kABytes, wn0 + j * MF, 0, lane);                             \
     }
-    // one stage: T uses fragment set CUR and reads stage T + 1 into set NXT;
-    // SYNC: the stage opens with the barrier (and the loads it allows)
-#define FCW4_STAGE(T, CUR, NXT, SYNC)                                                                        \
-    {                                                                                                        \
-        constexpr int nl_ = (SYNC) ? P * kLoads : 0;                                                         \
-        constexpr int gap_ = nl_ > 0 ? (TM * TN - kReads) / nl_ : 1;                                         \
-        if constexpr (SYNC) {                                                                                \
-            waitcnt<kInFlight, 0>();                                                                         \
-            __builtin_amdgcn_s_barrier();                                                                    \
-            __builtin_amdgcn_sched_barrier(0);                                                               \
-        }                                                                                                    \
-        FCW4_READ((T) + 1, NXT)                                                                              \
-        if constexpr (SYNC) {                                                                                \
-            if constexpr (P == 1) {                                                                          \
-                FCW4_ISSUE((T) + S)                                                                          \
-            } else {                                                                                         \
-                FCW4_ISSUE((T) + 3)                                                                          \
-                FCW4_ISSUE((T) + 4)                                                                          \
-            }                                                                                                \
-        }                                                                                                    \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j)        \
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[CUR][j], fa[CUR][i], acc[i][j], 0, 0, 0); \
-        _Pragma("unroll") for (int u = 0; u < TM * TN; ++u) {                                                \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                               \
-            if (u < kReads)                                                                                  \
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                           \
-            else if ((u - kReads) % gap_ == 0 && (u - kReads) / gap_ < nl_)                                  \
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                           \
-        }                                                                                                    \
-        __builtin_amdgcn_sched_barrier(0);                                                                   \
+    // stage T from fragment set CUR; reads stage T + 1 into set NXT
+#define FCW4_STAGE(T, CUR, NXT)                  \
+    {                                            \
+        waitcnt<kInFlight, 0>();                 \
+        __builtin_amdgcn_s_barrier();            \
+        __builtin_amdgcn_sched_barrier(0);       \
+        FCW4_READ((T) + 1, NXT)                  \
+        FCW4_ISSUE((T) + S)                      \
+        FCW4_MFMA_STEP(CUR)                      \
+        w4_interleave<kReads, kLoads>();         \
+        __builtin_amdgcn_sched_barrier(0);       \
     }
 
     if (nkt > 0) {
-        constexpr int kPrologue = P == 1 ? S : S - 1;  // stages requested before the loop
 #pragma unroll
-        for (int s = 0; s < kPrologue; ++s) FCW4_ISSUE(s)
-        waitcnt<(kPrologue - 1) * kLoads, 0>();
+        for (int s = 0; s < S; ++s) FCW4_ISSUE(s)
+        waitcnt<(S - 1) * kLoads, 0>();
         __builtin_amdgcn_s_barrier();
         FCW4_READ(0, 0)
         for (int t = 0; t < nkt; t += 2) {  // nkt is even: the reduction is a multiple of 64
-            FCW4_STAGE(t, 0, 1, true)
-            FCW4_STAGE(t + 1, 1, 0, P == 1)
+            FCW4_STAGE(t, 0, 1)
+            FCW4_STAGE(t + 1, 1, 0)
         }
-        waitcnt<0, 0>();  // drain the trailing (out-of-range) loads
+        waitcnt<0, 0>();  // drain the trailing prefetches
     }
 #undef FCW4_ISSUE
 #undef FCW4_READ
 #undef FCW4_STAGE
 
-    store_tile<MF, TM, TN, OUT_F32>(g, slice, m0, n0, wm0, wn0, lane, acc);
+    store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
 }
+
+// One v_mfma_f32_16x16x32_bf16 (B fragment as source A) whose accumulator is
+// pinned to AGPRs, and whose position relative to the loads, LDS reads and
+// barriers is its place in the source. The compiler's register allocator
+// otherwise moves 256 accumulators between AGPRs and VGPRs when a step issues
+// many loads. Hazards the compiler no longer sees are covered by the kernel:
+// an accumulator is read again only by the same MFMA 64 MFMAs later, sources
+// come from LDS reads the compiler waits for, and s_nops follow the zero
+// initialisation and precede the epilogue.
+__device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& b, const bf16x8& a) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+template <bool A_OC, bool B_OC, bool OUT_F32>
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64_kernel(
+    GemmArgs g) {
+    constexpr int MF = 16, BKP = 64;
+    constexpr int kABytes = 256 * BKP * 2;                                       // 32 KB per operand
+    constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;                                // 8
+    constexpr int kLoads = kLA + DmaPP<B_OC, BKP>::kInstr;                       // per wave per stage
+    constexpr int kGap = (64 - 16) / kLoads;                                     // MFMAs between loads
+    static_assert(kGap >= 1 && 16 + kGap * (kLoads - 1) < 64, "loads fit in one step");
+    // one array per slot and operand: the compiler tracks each array's
+    // direct-to-LDS writes separately, so an LDS read waits only for the
+    // loads into the array it reads
+    __shared__ __attribute__((aligned(1024))) char a0[kABytes];
+    __shared__ __attribute__((aligned(1024))) char b0[kABytes];
+    __shared__ __attribute__((aligned(1024))) char a1[kABytes];
+    __shared__ __attribute__((aligned(1024))) char b1[kABytes];
+
+    const W4Setup w = w4_setup<A_OC, B_OC, BKP>(g);
+    const int lane = w.lane, wave = w.wave, wm0 = w.wm0, wn0 = w.wn0, nkt = w.nkt;
+    DmaPP<A_OC, BKP> da;
+    DmaPP<B_OC, BKP> db;
+    da.init(wave, lane, g.lda, w.m0, g.M);
+    db.init(wave, lane, g.ldb, w.n0, g.N);
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 fa[2][8], fb[2][8];
+
+    // byte offsets of stage SIDX along the reduction (past the end: the last stage)
+#define FCW64_STEPS(SIDX)                                                                  \
+    const int64_t k0_ = w.kbeg + (int64_t)((SIDX) < nkt ? (SIDX) : nkt - 1) * BKP;         \
+    const uint32_t sa_ = (uint32_t)(A_OC ? k0_ * g.lda * 2 : k0_ * 2);                     \
+    const uint32_t sb_ = (uint32_t)(B_OC ? k0_ * g.ldb * 2 : k0_ * 2);
+#define FCW64_ISSUE(SA, SB, SIDX)                        \
+    {                                                    \
+        FCW64_STEPS(SIDX)                                \
+        da.issue_full(w.ra, SA, sa_, wave);              \
+        db.issue_full(w.rb, SB, sb_, wave);              \
+    }
+    // one 32-value step: 64 MFMAs from set CUR; after each of the first 16 the
+    // LDS read of one fragment of step KS of slot (RA, RB) into set NXT; with
+    // LOADS, the loads of stage LSTAGE into slot (LA, LB) spread over the rest
+#define FCW64_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, LSTAGE)                                        \
+    {                                                                                                  \
+        FCW64_STEPS(LSTAGE)                                                                            \
+        _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
+            mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
+            if (u < 8) {                                                                               \
+                fa[NXT][u] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + u * MF, KS, lane);                   \
+            } else if (u < 16) {                                                                       \
+                fb[NXT][u - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (u - 8) * MF, KS, lane);         \
+            } else if ((LOADS) && (u - 16) % kGap == 0 && (u - 16) / kGap < kLoads) {                  \
+                const int l_ = (u - 16) / kGap;                                                        \
+                if (l_ < kLA)                                                                          \
+                    da.issue_one(w.ra, LA, sa_, wave, l_);                                             \
+                else                                                                                   \
+                    db.issue_one(w.rb, LB, sb_, wave, l_ - kLA);                                       \
+            }                                                                                          \
+        }                                                                                              \
+    }
+    // stage T in slot (XA, XB), stage T + 1 in slot (YA, YB)
+#define FCW64_STAGE(T, XA, XB, YA, YB)                                 \
+    {                                                                  \
+        FCW64_STEP(0, 1, XA, XB, 1, false, XA, XB, T)                  \
+        waitcnt<0, 0>();                                               \
+        __builtin_amdgcn_s_barrier();                                  \
+        FCW64_STEP(1, 0, YA, YB, 0, true, XA, XB, (T) + 2)             \
+    }
+
+    if (nkt > 0) {
+        FCW64_ISSUE(a0, b0, 0)
+        FCW64_ISSUE(a1, b1, 1)
+        waitcnt<kLoads, 0>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(a0, wm0 + i * MF, 0, lane);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF>(b0, wn0 + j * MF, 0, lane);
+        asm volatile("s_nop 4" ::: "memory");  // zeroed accumulators before the first MFMA reads them
+        for (int t = 0; t < nkt; t += 2) {     // nkt is even: the reduction is a multiple of 128
+            FCW64_STAGE(t, a0, b0, a1, b1)
+            FCW64_STAGE(t + 1, a1, b1, a0, b0)
+        }
+        waitcnt<0, 0>();  // drain the trailing prefetches
+    }
+#undef FCW64_STEPS
+#undef FCW64_ISSUE
+#undef FCW64_STEP
+#undef FCW64_STAGE
+    // the last MFMAs must have written their results before the epilogue reads them
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
+}
+#undef FCW4_MFMA_STEP
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // instance the table below names.
-template __global__ void gemm_w4_kernel<false, false, false, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, false, false, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, true, false, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, true, false, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, false, false, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, false, false, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, true, false, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, true, false, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, false, true, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, false, true, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, true, true, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<false, true, true, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, false, true, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, false, true, 2>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, true, true, 1>(GemmArgs);
-template __global__ void gemm_w4_kernel<true, true, true, 2>(GemmArgs);
+#define FCW4_INST(AOC, BOC, F32)                                        \
+    template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);   \
+    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32>(GemmArgs);
+FCW4_INST(false, false, false)
+FCW4_INST(false, true, false)
+FCW4_INST(true, false, false)
+FCW4_INST(true, true, false)
+FCW4_INST(false, false, true)
+FCW4_INST(false, true, true)
+FCW4_INST(true, false, true)
+FCW4_INST(true, true, true)
+#undef FCW4_INST
 
 using KernelFn = void (*)(GemmArgs);
 struct W4Entry {
@@ -193,14 +305,14 @@ struct W4Entry {
     const char* name;
 };
 
-#define FCW4_K(AOC, BOC, F32, P) \
-    W4Entry { gemm_w4_kernel<AOC, BOC, F32, P>, "gemm_w4_kernel<" #AOC ", " #BOC ", " #F32 ", " #P ">" }
-#define FCW4_ALL(P)                                                                                  \
-    FCW4_K(false, false, false, P), FCW4_K(false, true, false, P), FCW4_K(true, false, false, P),     \
-        FCW4_K(true, true, false, P), FCW4_K(false, false, true, P), FCW4_K(false, true, true, P),    \
-        FCW4_K(true, false, true, P), FCW4_K(true, true, true, P)
-// [barrier every P stages, P - 1][out_f32][a_oc][b_oc]
-const W4Entry kW4[2][8] = {{FCW4_ALL(1)}, {FCW4_ALL(2)}};
+#define FCW4_K(KN, AOC, BOC, F32) \
+    W4Entry { KN<AOC, BOC, F32>, #KN "<" #AOC ", " #BOC ", " #F32 ">" }
+#define FCW4_ALL(KN)                                                                               \
+    FCW4_K(KN, false, false, false), FCW4_K(KN, false, true, false), FCW4_K(KN, true, false, false), \
+        FCW4_K(KN, true, true, false), FCW4_K(KN, false, false, true), FCW4_K(KN, false, true, true), \
+        FCW4_K(KN, true, false, true), FCW4_K(KN, true, true, true)
+// [variant][out_f32][a_oc][b_oc]
+const W4Entry kW4[2][8] = {{FCW4_ALL(gemm_w4_kernel)}, {FCW4_ALL(gemm_w4k64_kernel)}};
 
 const W4Entry& w4_entry(int variant, bool a_oc, bool b_oc, bool out_f32) {
     return kW4[variant & 1][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];

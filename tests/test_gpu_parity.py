@@ -139,9 +139,11 @@ def test_exact_power_of_two_scaled_inputs():
 
 
 # (320, 576, 192): every reduction length (576, 192, 320) is a multiple of 64,
-# so the kernels that take reduction stages in pairs run too, with ragged
-# output tiles and two- and four-way reduction splits.
-@pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192)],
+# so the kernels that take 32-value reduction stages in pairs run too, with
+# ragged output tiles and two- and four-way reduction splits. (384, 1024, 384):
+# every reduction a multiple of 128 (64-value stages in pairs), ragged tiles.
+@pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192),
+                                   (384, 1024, 384)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
