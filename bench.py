@@ -172,10 +172,10 @@ def run_per_launch(layers, steps, torch, F):
             a.record(stream)
             fn()
             b.record(stream)
-            recs.append((L, op, a, b))
+            recs.append((L, opname, op, a, b))
     torch.cuda.synchronize()
     out = {}
-    for L, op, a, b in recs:
+    for L, opname, op, a, b in recs:
         g = L.g
         desc = F.fc_plan_describe(op, g.M, g.K, g.N)
         key = desc["kernel"]
@@ -186,17 +186,29 @@ def run_per_launch(layers, steps, torch, F):
         # compulsory HBM bytes: both bf16 inputs once, the bf16 output once
         e["bytes"].append(2 * (g.M * g.K + g.K * g.N + g.M * g.N))
         e["single_launch"] = e["single_launch"] and single
+        e.setdefault("by_call", {}).setdefault((g.name, opname), []).append(a.elapsed_time(b))
     return out
 
 
-def plans_of(layers, F):
+def plans_of(layers, F, kern=None):
+    """The plan each call runs; with per-call timings, its mean time and rate inside the step."""
+    by_call = {}
+    for v in (kern or {}).values():
+        for key, ms in v.get("by_call", {}).items():
+            by_call.setdefault(key, []).extend(ms)
     res = []
     for L in layers:
         g = L.g
         for opname, op, _ in L.calls():
             d = F.fc_plan_describe(op, g.M, g.K, g.N)
-            res.append({"gemm": g.name, "op": opname, "M": g.M, "K": g.K, "N": g.N, "kernel": d["kernel"],
-                        "split": d["split"], "copy": d["copy"]})
+            rec = {"gemm": g.name, "op": opname, "M": g.M, "K": g.K, "N": g.N, "kernel": d["kernel"],
+                   "split": d["split"], "copy": d["copy"]}
+            ms = by_call.get((g.name, opname))
+            if ms:
+                avg = sum(ms) / len(ms)
+                rec["avg_us"] = round(avg * 1e3, 2)
+                rec["tflops"] = round(g.flops / (avg / 1e3) / 1e12, 1)
+            res.append(rec)
     return res
 
 
@@ -348,7 +360,7 @@ def main():
                           "min": round(float(np.min(per_step)), 4), "max": round(float(np.max(per_step)), 4)},
         "roofline": roofline,
         "per_kernel": per_kernel,
-        "plans": plans_of(layers, F),
+        "plans": plans_of(layers, F, kern),
         "tune_s": round(tune_s, 2),
         "kernel_source_hash": kernel_source_hash(),
         "device": props.name,

@@ -215,8 +215,12 @@ int default_plan(const Problem& p) {
             break;
         }
     }
-    // 256x256 tiles filling the chip: the 8-wave ping-pong kernel; otherwise
-    // the 4-wave pipelined kernel with the largest tile that still does
+    // 256x256 tiles filling the chip: the one-wave-per-SIMD kernel with
+    // 64-value stages when the reduction allows it, else the 8-wave
+    // ping-pong kernel; otherwise the 4-wave pipelined kernel with the
+    // largest tile that still fills the chip
+    const int w64 = encode_plan(0, 0, 0, kFamilyW4 + 1);
+    if (tile == 0 && plan_applies(p, decode_plan(w64))) return w64;
     const int pp = encode_plan(0, 0, 0, 4);  // two-barrier ping-pong, 16x16x32
     if (tile == 0 && plan_applies(p, decode_plan(pp))) return pp;
     const int pipe = encode_plan(tile, 0, 0, 0);

@@ -156,10 +156,14 @@ struct DmaPP {
     }
 
     // Load instruction j alone of issue_full (for hand-interleaved schedules).
+    // The stage offset goes in the scalar offset (no per-load vector add):
+    // callers clamp stages to the reduction range, so in-range lanes stay
+    // inside the operand, and rows past the matrix keep their out-of-range
+    // vector offset (kOOB + step < 2^32 stays past the buffer either way).
     __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rsrc, char* region, uint32_t step, int wq,
                                               int j) const {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(region + (wq * kInstr + j) * 1024), 16,
-                                                 base[j] + step, 0, 0, 0);
+                                                 base[j], step, 0, 0);
     }
 
     // Same loads for a stage that lies wholly inside the reduction range (no

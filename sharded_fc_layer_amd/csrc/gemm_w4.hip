@@ -169,6 +169,31 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
 }
 
+// Placement of a 64-MFMA step's 16 fragment reads and NL loads: the index of
+// the read (0..15) or load (0..NL-1) issued right after MFMA u, or -1.
+// 0: reads after MFMAs 0..15, then the loads evenly over the rest;
+// 1: the loads first, after every second MFMA, then the reads;
+// 2: one load after every fourth MFMA, reads after the two that follow;
+// 3: as 2 with a load after every third MFMA and one read after the next;
+// 4: as 2, and a step without loads spreads its reads over every second MFMA.
+__device__ constexpr int w64_read_after(int sched, int nl, int u) {
+    if (nl == 0) return sched == 4 ? ((u % 2 == 0 && u / 2 < 16) ? u / 2 : -1) : (u < 16 ? u : -1);
+    if (sched == 0) return u < 16 ? u : -1;
+    if (sched == 1) return (u >= 2 * nl && u < 2 * nl + 16) ? u - 2 * nl : -1;
+    if (sched == 3) return (u % 3 == 1 && u / 3 < 16) ? u / 3 : -1;
+    return (u % 4 != 0 && u % 4 != 3 && u / 4 < 8) ? 2 * (u / 4) + (u % 4) - 1 : -1;
+}
+__device__ constexpr int w64_load_after(int sched, int nl, int u) {
+    if (nl == 0) return -1;
+    if (sched == 0) {
+        const int gap = 48 / nl;
+        return (u >= 16 && (u - 16) % gap == 0 && (u - 16) / gap < nl) ? (u - 16) / gap : -1;
+    }
+    if (sched == 1) return (u % 2 == 0 && u / 2 < nl) ? u / 2 : -1;
+    if (sched == 3) return (u % 3 == 0 && u / 3 < nl) ? u / 3 : -1;
+    return (u % 4 == 0 && u / 4 < nl) ? u / 4 : -1;
+}
+
 // One v_mfma_f32_16x16x32_bf16 (B fragment as source A) whose accumulator is
 // pinned to AGPRs, and whose position relative to the loads, LDS reads and
 // barriers is its place in the source. The compiler's register allocator
@@ -188,8 +213,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     constexpr int kABytes = 256 * BKP * 2;                                       // 32 KB per operand
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;                                // 8
     constexpr int kLoads = kLA + DmaPP<B_OC, BKP>::kInstr;                       // per wave per stage
-    constexpr int kGap = (64 - 16) / kLoads;                                     // MFMAs between loads
-    static_assert(kGap >= 1 && 16 + kGap * (kLoads - 1) < 64, "loads fit in one step");
+    constexpr int kSched = 2;  // placement of reads and loads in a step (w64_read_after)
+    constexpr bool kSplitLoads = false;  // a stage's loads over two steps (slower: too little time to land)
     // one array per slot and operand: the compiler tracks each array's
     // direct-to-LDS writes separately, so an LDS read waits only for the
     // loads into the array it reads
@@ -224,39 +249,52 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         db.issue_full(w.rb, SB, sb_, wave);              \
     }
     // one 32-value step: 64 MFMAs from set CUR; after each of the first 16 the
-    // LDS read of one fragment of step KS of slot (RA, RB) into set NXT; with
-    // LOADS, the loads of stage LSTAGE into slot (LA, LB) spread over the rest
+    // LDS read of one fragment of step KS of slot (RA, RB) into set NXT; then
+    // the loads LOADS selects (bit 0: operand A into LA, bit 1: operand B into
+    // LB) of stage LSTAGE, spread evenly over the remaining MFMAs
 #define FCW64_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, LSTAGE)                                        \
     {                                                                                                  \
         FCW64_STEPS(LSTAGE)                                                                            \
+        constexpr int la_ = ((LOADS) & 1) ? kLA : 0;                                                   \
+        constexpr int nl_ = la_ + (((LOADS) & 2) ? kLoads - kLA : 0);                                  \
         _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
             mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
-            if (u < 8) {                                                                               \
-                fa[NXT][u] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + u * MF, KS, lane);                   \
-            } else if (u < 16) {                                                                       \
-                fb[NXT][u - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (u - 8) * MF, KS, lane);         \
-            } else if ((LOADS) && (u - 16) % kGap == 0 && (u - 16) / kGap < kLoads) {                  \
-                const int l_ = (u - 16) / kGap;                                                        \
-                if (l_ < kLA)                                                                          \
-                    da.issue_one(w.ra, LA, sa_, wave, l_);                                             \
-                else                                                                                   \
-                    db.issue_one(w.rb, LB, sb_, wave, l_ - kLA);                                       \
+            const int r_ = w64_read_after(kSched, nl_, u);                                              \
+            if (r_ >= 0 && r_ < 8) {                                                                   \
+                fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
+            } else if (r_ >= 8) {                                                                      \
+                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
             }                                                                                          \
+            const int l_ = w64_load_after(kSched, nl_, u);                                             \
+            if (l_ >= 0 && l_ < la_)                                                                   \
+                da.issue_one(w.ra, LA, sa_, wave, l_);                                                 \
+            else if (l_ >= la_)                                                                        \
+                db.issue_one(w.rb, LB, sb_, wave, l_ - la_);                                           \
         }                                                                                              \
     }
-    // stage T in slot (XA, XB), stage T + 1 in slot (YA, YB)
-#define FCW64_STAGE(T, XA, XB, YA, YB)                                 \
-    {                                                                  \
-        FCW64_STEP(0, 1, XA, XB, 1, false, XA, XB, T)                  \
-        waitcnt<0, 0>();                                               \
-        __builtin_amdgcn_s_barrier();                                  \
-        FCW64_STEP(1, 0, YA, YB, 0, true, XA, XB, (T) + 2)             \
+    // stage T in slot (XA, XB), stage T + 1 in slot (YA, YB). Step 1 opens with
+    // the barrier that certifies stage T + 1 and frees slot X (its last reads,
+    // of step 1, were issued during step 0). kSplitLoads: the A half of stage
+    // T + 2 is loaded during step 1 and its B half during step 0 of stage
+    // T + 1 (slot Y's B tile is free since the barrier of stage T - 1), which
+    // halves the address unit's load rate; otherwise both halves in step 1.
+#define FCW64_STAGE(T, XA, XB, YA, YB)                                                    \
+    {                                                                                     \
+        FCW64_STEP(0, 1, XA, XB, 1, kSplitLoads ? 2 : 0, YA, YB, (T) + 1)                 \
+        waitcnt<0, 0>();                                                                  \
+        __builtin_amdgcn_s_barrier();                                                     \
+        FCW64_STEP(1, 0, YA, YB, 0, kSplitLoads ? 1 : 3, XA, XB, (T) + 2)                 \
     }
 
     if (nkt > 0) {
         FCW64_ISSUE(a0, b0, 0)
-        FCW64_ISSUE(a1, b1, 1)
-        waitcnt<kLoads, 0>();
+        if constexpr (kSplitLoads) {
+            FCW64_STEPS(1)
+            da.issue_full(w.ra, a1, sa_, wave);
+        } else {
+            FCW64_ISSUE(a1, b1, 1)
+        }
+        waitcnt<kSplitLoads ? kLA : kLoads, 0>();
         __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(a0, wm0 + i * MF, 0, lane);
