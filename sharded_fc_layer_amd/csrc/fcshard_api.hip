@@ -131,7 +131,7 @@ bool plan_applies(const Problem& p, const Plan& pl) {
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
     if (pl.family >= 2 && pl.tile != 0) return false;
     if (pl.family >= kFamilyW4) {  // stages run in pairs, no odd tail: every slice a multiple of 64 or 128
-        const int64_t q = pl.family == kFamilyW4 ? 64 : 128;
+        const int64_t q = pl.family == kFamilyW4 + 1 ? 128 : 64;
         int64_t ks;
         int slices;
         split_geometry(p.K, pl.split, &ks, &slices);

@@ -194,6 +194,19 @@ __device__ constexpr int w64_load_after(int sched, int nl, int u) {
     return (u % 4 == 0 && u / 4 < nl) ? u / 4 : -1;
 }
 
+// Orders every compiler write of the accumulators (their zero
+// initialisation, copies where control paths merge) before the asm MFMAs
+// that read them: every accumulator passes through an empty asm (so such
+// writes must come before it), then a few wait states pass before the next
+// MFMA.
+__device__ __forceinline__ void w4_acc_fence(f32x4 (&acc)[8][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+    asm volatile("s_nop 4" ::: "memory");
+}
+
 // One v_mfma_f32_16x16x32_bf16 (B fragment as source A) whose accumulator is
 // pinned to AGPRs, and whose position relative to the loads, LDS reads and
 // barriers is its place in the source. The compiler's register allocator
@@ -242,6 +255,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int64_t k0_ = w.kbeg + (int64_t)((SIDX) < nkt ? (SIDX) : nkt - 1) * BKP;         \
     const uint32_t sa_ = (uint32_t)(A_OC ? k0_ * g.lda * 2 : k0_ * 2);                     \
     const uint32_t sb_ = (uint32_t)(B_OC ? k0_ * g.ldb * 2 : k0_ * 2);
+
 #define FCW64_ISSUE(SA, SB, SIDX)                        \
     {                                                    \
         FCW64_STEPS(SIDX)                                \
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(a0, wm0 + i * MF, 0, lane);
 #pragma unroll
         for (int j = 0; j < 8; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF>(b0, wn0 + j * MF, 0, lane);
-        asm volatile("s_nop 4" ::: "memory");  // zeroed accumulators before the first MFMA reads them
+        w4_acc_fence(acc);  // zeroed accumulators before the first MFMA reads them
         for (int t = 0; t < nkt; t += 2) {     // nkt is even: the reduction is a multiple of 128
             FCW64_STAGE(t, a0, b0, a1, b1)
             FCW64_STAGE(t + 1, a1, b1, a0, b0)
@@ -324,8 +338,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // instance the table below names.
-#define FCW4_INST(AOC, BOC, F32)                                        \
-    template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);   \
+#define FCW4_INST(AOC, BOC, F32)                                          \
+    template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);     \
     template __global__ void gemm_w4k64_kernel<AOC, BOC, F32>(GemmArgs);
 FCW4_INST(false, false, false)
 FCW4_INST(false, true, false)
