@@ -38,9 +38,10 @@ constexpr int kNumSplits = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // 0: 4-wave pipelined, 1: simple, 2-5: 8-wave ping-pong (256 x 256), variant
 // = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
-// 6, 7: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
-// 32-value (6) or 64-value (7) reduction stages
-constexpr int kNumFamilies = 8;
+// 6-8: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
+// 32-value stages (6), 64-value stages in two LDS slots (7) or in a ring of
+// three A and two B tiles (8)
+constexpr int kNumFamilies = 9;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
@@ -50,7 +51,7 @@ struct Plan {
     int tile;
     int split;   // number of reduction slices requested
     int copy;    // bit mask
-    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-7 one wave per SIMD
+    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-8 one wave per SIMD
 };
 
 Plan decode_plan(int id) {
@@ -130,8 +131,8 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
     if (pl.family >= 2 && pl.tile != 0) return false;
-    if (pl.family >= kFamilyW4) {  // stages run in pairs, no odd tail: every slice a multiple of 64 or 128
-        const int64_t q = pl.family == kFamilyW4 + 1 ? 128 : 64;
+    if (pl.family >= kFamilyW4) {  // whole stages (pairs of 32- or 64-value stages for 6 and 7)
+        const int64_t q = pl.family == kFamilyW4 ? 64 : pl.family == kFamilyW4 + 1 ? 128 : 64;
         int64_t ks;
         int slices;
         split_geometry(p.K, pl.split, &ks, &slices);

@@ -61,7 +61,9 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 // per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
 // launch_gemm_pipe, and K a multiple of 64, of 128 for variant 1).
 // variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
-// 2 slots (whole-cache-line rows for reduction-contiguous operands).
+// 2 slots (whole-cache-line rows for reduction-contiguous operands); 2: the
+// same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about
+// two stages to land.
 hipError_t launch_gemm_w4(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream);
 const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);

@@ -207,6 +207,17 @@ __device__ __forceinline__ void w4_acc_fence(f32x4 (&acc)[8][8]) {
     asm volatile("s_nop 4" ::: "memory");
 }
 
+// The last MFMAs must have written their results before anything else
+// reads the accumulators: wait states, then every accumulator through an
+// empty asm (reads of them come after it).
+__device__ __forceinline__ void w4_acc_drain(f32x4 (&acc)[8][8]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
 // One v_mfma_f32_16x16x32_bf16 (B fragment as source A) whose accumulator is
 // pinned to AGPRs, and whose position relative to the loads, LDS reads and
 // barriers is its place in the source. The compiler's register allocator
@@ -325,12 +336,131 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCW64_ISSUE
 #undef FCW64_STEP
 #undef FCW64_STAGE
-    // the last MFMAs must have written their results before the epilogue reads them
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    w4_acc_drain(acc);  // the last MFMAs must have written their results before the epilogue reads them
+
+    store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
+}
+// gemm_w4k64r_kernel: the 64-value stages of gemm_w4k64_kernel in the whole
+// 160 KB LDS, as a ring of three A tiles and two B tiles (32 KB each, one
+// array each). Step 1 of stage t opens with the barrier that certifies stage
+// t + 1 and frees stage t's tiles; it then loads the B tile of stage t + 2
+// (into stage t's B tile) and the A tile of stage t + 3 (into stage t's A
+// tile), so A loads have three steps to land and B loads at least one and a
+// half. The loop body holds one period of six stages with every tile fixed
+// (stage t in A tile t mod 3 and B tile t mod 2), and the control flow stays
+// that one loop: a stage count that is not a multiple of 6 is padded at the
+// front with virtual stages of zeros (up to five stages of extra MFMA work;
+// the tuner weighs it against gemm_w4k64_kernel).
+template <bool A_OC, bool B_OC, bool OUT_F32>
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
+    GemmArgs g) {
+    constexpr int MF = 16, BKP = 64;
+    constexpr int kT = 256 * BKP * 2;  // 32 KB per operand tile
+    constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
+    constexpr int kLB = DmaPP<B_OC, BKP>::kInstr;
+    constexpr int kSched = 2;
+    __shared__ __attribute__((aligned(1024))) char ta0[kT];
+    __shared__ __attribute__((aligned(1024))) char ta1[kT];
+    __shared__ __attribute__((aligned(1024))) char ta2[kT];
+    __shared__ __attribute__((aligned(1024))) char tb0[kT];
+    __shared__ __attribute__((aligned(1024))) char tb1[kT];
+
+    const W4Setup w = w4_setup<A_OC, B_OC, BKP>(g);
+    const int lane = w.lane, wave = w.wave, wm0 = w.wm0, wn0 = w.wn0, nkt = w.nkt;
+    DmaPP<A_OC, BKP> da;
+    DmaPP<B_OC, BKP> db;
+    da.init(wave, lane, g.lda, w.m0, g.M);
+    db.init(wave, lane, g.ldb, w.n0, g.N);
+
+    f32x4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 fa[2][8], fb[2][8];
+
+#define FCR_TA(I) ((I) == 0 ? ta0 : (I) == 1 ? ta1 : ta2)
+#define FCR_TB(I) ((I) == 0 ? tb0 : tb1)
+#define FCR_OFF(SIDX) (w.kbeg + (int64_t)((SIDX) < 0 ? 0 : (SIDX) < nkt ? (SIDX) : nkt - 1) * BKP)
+#define FCR_STEP_A(SIDX) (uint32_t)(A_OC ? FCR_OFF(SIDX) * g.lda * 2 : FCR_OFF(SIDX) * 2)
+#define FCR_STEP_B(SIDX) (uint32_t)(B_OC ? FCR_OFF(SIDX) * g.ldb * 2 : FCR_OFF(SIDX) * 2)
+#define FCR_RA(SIDX) ((SIDX) < 0 ? rza : w.ra)
+#define FCR_RB(SIDX) ((SIDX) < 0 ? rzb : w.rb)
+    // 64 MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
+    // set NXT; with LOADS, the B tile of stage T + 2 into LB, then the A tile
+    // of stage T + 3 into LA, placed as w64_read_after / w64_load_after say
+#define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, T)                                              \
+    {                                                                                                  \
+        const uint32_t sb_ = FCR_STEP_B((T) + 2), sa_ = FCR_STEP_A((T) + 3);                           \
+        const __amdgpu_buffer_rsrc_t rb_ = FCR_RB((T) + 2), ra_ = FCR_RA((T) + 3);                     \
+        constexpr int nl_ = (LOADS) ? kLA + kLB : 0;                                                   \
+        _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
+            mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
+            const int r_ = w64_read_after(kSched, nl_, u);                                             \
+            if (r_ >= 0 && r_ < 8) {                                                                   \
+                fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
+            } else if (r_ >= 8) {                                                                      \
+                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
+            }                                                                                          \
+            const int l_ = w64_load_after(kSched, nl_, u);                                             \
+            if (l_ >= 0 && l_ < kLB)                                                                   \
+                db.issue_one(rb_, LB, sb_, wave, l_);                                                  \
+            else if (l_ >= kLB)                                                                        \
+                da.issue_one(ra_, LA, sa_, wave, l_ - kLB);                                            \
+        }                                                                                              \
+    }
+    // stage T with A tile P mod 3 and B tile P mod 2 (P = T mod 6): step 0,
+    // the barrier (only the A loads of the last step may still be in
+    // flight), step 1 (reads step 0 of stage T + 1)
+#define FCR_STAGE(P, T)                                                                                \
+    {                                                                                                  \
+        FCR_STEP(0, 1, FCR_TA((P) % 3), FCR_TB((P) % 2), 1, false, ta0, tb0, T)                        \
+        waitcnt<kLA, 0>();                                                                             \
+        __builtin_amdgcn_s_barrier();                                                                  \
+        FCR_STEP(1, 0, FCR_TA(((P) + 1) % 3), FCR_TB(((P) + 1) % 2), 0, true, FCR_TA((P) % 3),         \
+                 FCR_TB((P) % 2), T)                                                                   \
+    }
+
+    if (nkt > 0) {
+        // The loop runs whole periods of six stages: pad virtual stages
+        // -pad .. -1 go first and load through zero-size descriptors, so
+        // their tiles hold zeros and their MFMAs add nothing.
+        const int pad = (6 - nkt % 6) % 6;
+        const __amdgpu_buffer_rsrc_t rza = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, 0, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rzb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, 0, 0, kRsrcWord3);
+        // stages -pad, -pad + 1 and the A tile of -pad + 2; wait for the first; read its step 0
+        da.issue_full(FCR_RA(-pad), ta0, FCR_STEP_A(-pad), wave);
+        db.issue_full(FCR_RB(-pad), tb0, FCR_STEP_B(-pad), wave);
+        da.issue_full(FCR_RA(1 - pad), ta1, FCR_STEP_A(1 - pad), wave);
+        db.issue_full(FCR_RB(1 - pad), tb1, FCR_STEP_B(1 - pad), wave);
+        da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
+        waitcnt<2 * kLA + kLB, 0>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF>(tb0, wn0 + j * MF, 0, lane);
+        w4_acc_fence(acc);
+        for (int t = -pad; t < nkt; t += 6) {  // nkt + pad is a multiple of 6
+            FCR_STAGE(0, t)
+            FCR_STAGE(1, t + 1)
+            FCR_STAGE(2, t + 2)
+            FCR_STAGE(3, t + 3)
+            FCR_STAGE(4, t + 4)
+            FCR_STAGE(5, t + 5)
+        }
+        waitcnt<0, 0>();  // drain the trailing prefetches
+    }
+#undef FCR_TA
+#undef FCR_TB
+#undef FCR_OFF
+#undef FCR_STEP_A
+#undef FCR_STEP_B
+#undef FCR_RA
+#undef FCR_RB
+#undef FCR_STEP
+#undef FCR_STAGE
+    w4_acc_drain(acc);  // the last MFMAs must have written their results before the epilogue reads them
 
     store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
 }
@@ -340,7 +470,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 // instance the table below names.
 #define FCW4_INST(AOC, BOC, F32)                                          \
     template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);     \
-    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32>(GemmArgs);
+    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32>(GemmArgs);  \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32>(GemmArgs);
 FCW4_INST(false, false, false)
 FCW4_INST(false, true, false)
 FCW4_INST(true, false, false)
@@ -364,10 +495,11 @@ struct W4Entry {
         FCW4_K(KN, true, true, false), FCW4_K(KN, false, false, true), FCW4_K(KN, false, true, true), \
         FCW4_K(KN, true, false, true), FCW4_K(KN, true, true, true)
 // [variant][out_f32][a_oc][b_oc]
-const W4Entry kW4[2][8] = {{FCW4_ALL(gemm_w4_kernel)}, {FCW4_ALL(gemm_w4k64_kernel)}};
+const W4Entry kW4[3][8] = {{FCW4_ALL(gemm_w4_kernel)}, {FCW4_ALL(gemm_w4k64_kernel)},
+                           {FCW4_ALL(gemm_w4k64r_kernel)}};
 
 const W4Entry& w4_entry(int variant, bool a_oc, bool b_oc, bool out_f32) {
-    return kW4[variant & 1][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
+    return kW4[variant < 0 || variant > 2 ? 0 : variant][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
 }
 
 }  // namespace
