@@ -95,9 +95,13 @@ fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY,
 
 /*
  * Times candidate plans of all three products at (M, K, N, x_order, w_order,
- * out_dtype) on `stream` and caches the fastest per product. flags: 0 =
- * quick search, 1 = exhaustive. Allocates temporary buffers and may grow the
- * workspace; synchronizes `stream`. Plans are kept until fc_release.
+ * out_dtype) on `stream` and caches the fastest per product. flags bit 0:
+ * exhaustive search (else quick); bit 1: time with warm caches. By default
+ * every timed launch follows a 512 MB copy that evicts the L2s and the MALL,
+ * so plans are ranked on operands read from HBM, as in a training step
+ * (warm caches are used if those buffers cannot be allocated). Allocates
+ * temporary buffers and may grow the workspace; synchronizes `stream`.
+ * Plans are kept until fc_release.
  */
 fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
                   fc_out_dtype out_dtype, int flags, void* stream);

@@ -423,13 +423,38 @@ struct TuneBuffers {
     }
 };
 
+// Two 256 MB buffers; a transpose of one into the other streams 512 MB through
+// the L2s and the 256 MB MALL, so the GEMM timed after it reads its operands
+// from HBM, as a training step does (each shard GEMM's operands were last
+// touched several GEMMs earlier).
+struct CacheFlush {
+    static constexpr int64_t kRows = 16384, kCols = 8192;  // 2 B each: 256 MB
+    uint16_t* a = nullptr;
+    uint16_t* b = nullptr;
+    bool init(hipStream_t s) {
+        if (hipMalloc(&a, kRows * kCols * 2) != hipSuccess || hipMalloc(&b, kRows * kCols * 2) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        return launch_fill_bf16(a, kRows * kCols, 7u, s) == hipSuccess;
+    }
+    hipError_t run(hipStream_t s) const { return launch_transpose_bf16(a, b, kRows, kCols, s); }
+    ~CacheFlush() {
+        if (a) hipFree(a);
+        if (b) hipFree(b);
+    }
+};
+
+// Median of `reps` single-launch times after `warm` untimed launches; with
+// `flush`, the caches are flushed before every timed launch.
 float time_plan(const Problem& p, const Plan& pl, void* ws, hipStream_t s, int warm, int reps, hipEvent_t* ev,
-                bool* ok) {
+                const CacheFlush* flush, bool* ok) {
     *ok = true;
     for (int i = 0; i < warm; ++i)
         if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
     std::vector<float> t;
     for (int i = 0; i < reps && *ok; ++i) {
+        if (flush && flush->run(s) != hipSuccess) *ok = false;
         hipEventRecord(ev[0], s);
         if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
         hipEventRecord(ev[1], s);
@@ -547,6 +572,14 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
     if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) return FC_E_HIP;
     const bool exhaustive = (flags & 1) != 0;
     const int warm = exhaustive ? 3 : 2, reps = exhaustive ? 10 : 5;
+    CacheFlush flush_bufs;
+    const CacheFlush* flush = nullptr;
+    if (!(flags & 2)) {
+        if (flush_bufs.init(s))
+            flush = &flush_bufs;
+        else if (log_enabled())
+            std::fprintf(stderr, "[fcshard] tune: no memory for the cache flush; timing with warm caches\n");
+    }
     fc_status result = FC_OK;
 
     for (int op = 0; op < 3; ++op) {
@@ -588,7 +621,7 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         std::vector<std::pair<int, float>> times;
         for (int id : cand) {
             bool ok;
-            const float ms = time_plan(p, decode_plan(id), ws, s, warm, reps, ev, &ok);
+            const float ms = time_plan(p, decode_plan(id), ws, s, warm, reps, ev, flush, &ok);
             if (!ok) {
                 (void)hipGetLastError();
                 continue;

@@ -148,10 +148,11 @@ def fc_bwd_weight(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16
 
 
 def fc_tune(M: int, K: int, N: int, x_order: int = ROW, w_order: int = ROW, out_dtype: int = OUT_BF16,
-            exhaustive: bool = False, stream=None) -> None:
-    """Time candidate plans of the three products at this shape and cache the fastest."""
-    _check(lib().fc_tune(M, K, N, x_order, w_order, out_dtype, 1 if exhaustive else 0, _stream(stream)),
-           "fc_tune")
+            exhaustive: bool = False, warm_caches: bool = False, stream=None) -> None:
+    """Time candidate plans of the three products at this shape and cache the fastest
+    (with caches flushed before each timed launch unless warm_caches)."""
+    flags = (1 if exhaustive else 0) | (2 if warm_caches else 0)
+    _check(lib().fc_tune(M, K, N, x_order, w_order, out_dtype, flags, _stream(stream)), "fc_tune")
 
 
 def fc_plan_count() -> int:
