@@ -121,21 +121,26 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
 /*
  * Describes the plan a hot call at this key would run: writes a NUL-terminated
  * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> ws=<bytes>"
- * into buf (truncated to len). Returns FC_E_INVALID for bad arguments.
+ * into buf (truncated to len), followed by " tuned_ms=<t>" when fc_tune chose
+ * the plan (or a loaded plan file recorded its time): the median time of one
+ * launch, in ms, as fc_tune measured it. Returns FC_E_INVALID for bad
+ * arguments.
  */
 fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order,
                            fc_order w_order, fc_out_dtype out_dtype, char* buf, size_t len);
 
 /*
  * Writes every cached plan of the current device to a text file, one line
- * "<arch> <op> <M> <K> <N> <x_order> <w_order> <out_dtype> <plan_id>".
+ * "<arch> <op> <M> <K> <N> <x_order> <w_order> <out_dtype> <plan_id>", plus
+ * " <ms>" (fc_tune's measured time) for plans that fc_tune chose.
  * FC_E_INVALID if path is NULL or the file cannot be written.
  */
 fc_status fc_plans_save(const char* path);
 
 /*
- * Reads such a file and caches, for the current device, every line whose
- * arch matches it (growing the workspace as the plans need). Lines for other
+ * Reads such a file (the time field is optional) and caches, for the current
+ * device, every line whose arch matches it, with its time if the line has
+ * one (growing the workspace as the plans need). Lines for other
  * archs are skipped. FC_E_INVALID if the file cannot be read or a line is
  * malformed (entries before it stay loaded).
  */

@@ -172,8 +172,15 @@ struct DevState {
     int64_t ws_bytes = 0;
 };
 
+// A cached plan and, when fc_tune chose it, its measured time (median of the
+// timed launches, ms); -1 when the plan was set or loaded without a time.
+struct PlanEntry {
+    int id;
+    float ms;
+};
+
 std::mutex g_mu;
-std::map<Key, int> g_plans;
+std::map<Key, PlanEntry> g_plans;
 DevState g_dev[kMaxDevices];
 
 bool log_enabled() {
@@ -355,7 +362,7 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
         if ((st = check_device(&dev)) != FC_OK) return st;
         int id = -1;
         auto it = g_plans.find(make_key(dev, op, M, K, N, xo, wo, dtype));
-        if (it != g_plans.end()) id = it->second;
+        if (it != g_plans.end()) id = it->second.id;
         if (id >= 0) {
             pl = decode_plan(id);
             // a plan that no longer applies (alignment) or lacks workspace falls back
@@ -364,6 +371,9 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
         if (id < 0) pl = decode_plan(default_plan(p));
         ws = g_dev[dev].ws;
     }
+    // the launchers report hipGetLastError(): drop an error that an earlier,
+    // unrelated HIP call of this thread left behind
+    (void)hipGetLastError();
     return run_plan(p, pl, ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
 }
 
@@ -517,7 +527,7 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
     const Plan pl = decode_plan(plan_id);
     if (!plan_applies(p, pl)) return FC_E_UNSUPPORTED;
     if ((st = grow_workspace(dev, ws_layout(p, pl).total)) != FC_OK) return st;
-    g_plans[key] = plan_id;
+    g_plans[key] = PlanEntry{plan_id, -1.0f};
     return FC_OK;
 }
 
@@ -536,11 +546,17 @@ fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x
     p.A = p.B = nullptr;
     p.C = nullptr;
     int id = -1;
+    float ms = -1.0f;
     auto it = g_plans.find(make_key(dev, op, M, K, N, x_order, w_order, out_dtype));
-    if (it != g_plans.end()) id = it->second;
-    if (id >= 0 && ws_layout(p, decode_plan(id)).total > g_dev[dev].ws_bytes) id = -1;
+    if (it != g_plans.end()) id = it->second.id, ms = it->second.ms;
+    if (id >= 0 && ws_layout(p, decode_plan(id)).total > g_dev[dev].ws_bytes) id = -1, ms = -1.0f;
     if (id < 0) id = default_plan(p);
-    const std::string s = describe(p, id, g_dev[dev].ws_bytes);
+    std::string s = describe(p, id, g_dev[dev].ws_bytes);
+    if (ms >= 0.0f) {
+        char t[48];
+        std::snprintf(t, sizeof t, " tuned_ms=%.6f", ms);
+        s += t;
+    }
     std::snprintf(buf, len, "%s", s.c_str());
     return FC_OK;
 }
@@ -556,6 +572,7 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         fc_status st = check_device(&dev);
         if (st != FC_OK) return st;
     }
+    (void)hipGetLastError();  // as in hot_call: no stale error from an earlier HIP call
     TuneBuffers b;
     const int64_t esz = out_dtype == FC_OUT_F32 ? 4 : 2;
     const int64_t out_elems = std::max(M * N, std::max(M * K, K * N));
@@ -564,10 +581,13 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         (void)hipGetLastError();
         return FC_E_NOMEM;
     }
-    if (launch_fill_bf16((uint16_t*)b.X, M * K, 1u, s) != hipSuccess ||
-        launch_fill_bf16((uint16_t*)b.W, K * N, 2u, s) != hipSuccess ||
-        launch_fill_bf16((uint16_t*)b.dY, M * N, 3u, s) != hipSuccess)
+    hipError_t fe = launch_fill_bf16((uint16_t*)b.X, M * K, 1u, s);
+    if (fe == hipSuccess) fe = launch_fill_bf16((uint16_t*)b.W, K * N, 2u, s);
+    if (fe == hipSuccess) fe = launch_fill_bf16((uint16_t*)b.dY, M * N, 3u, s);
+    if (fe != hipSuccess) {
+        if (log_enabled()) std::fprintf(stderr, "[fcshard] tune: filling the operands failed: %s\n", hipGetErrorString(fe));
         return FC_E_HIP;
+    }
     hipEvent_t ev[2];
     if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) return FC_E_HIP;
     const bool exhaustive = (flags & 1) != 0;
@@ -646,8 +666,11 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
             std::fprintf(stderr, "[fcshard] tune op=%d pick %s\n", op, pick >= 0 ? describe(p, pick, 0).c_str() : "none");
         }
         if (pick >= 0) {
+            float pick_ms = -1.0f;
+            for (auto& t : times)
+                if (t.first == pick) pick_ms = t.second;
             std::lock_guard<std::mutex> lk(g_mu);
-            g_plans[make_key(dev, op, M, K, N, x_order, w_order, out_dtype)] = pick;
+            g_plans[make_key(dev, op, M, K, N, x_order, w_order, out_dtype)] = PlanEntry{pick, pick_ms};
         }
     }
     hipEventDestroy(ev[0]);
@@ -667,8 +690,10 @@ fc_status fc_plans_save(const char* path) {
     for (const auto& kv : g_plans) {
         const Key& k = kv.first;
         if (k.dev != dev) continue;
-        std::fprintf(f, "%s %d %lld %lld %lld %d %d %d %d\n", g_dev[dev].arch, k.op, (long long)k.M, (long long)k.K,
-                     (long long)k.N, k.xo, k.wo, k.f32, kv.second);
+        std::fprintf(f, "%s %d %lld %lld %lld %d %d %d %d", g_dev[dev].arch, k.op, (long long)k.M, (long long)k.K,
+                     (long long)k.N, k.xo, k.wo, k.f32, kv.second.id);
+        if (kv.second.ms >= 0.0f) std::fprintf(f, " %.6f", kv.second.ms);
+        std::fputc('\n', f);
     }
     return std::fclose(f) == 0 ? FC_OK : FC_E_INVALID;
 }
@@ -689,8 +714,11 @@ fc_status fc_plans_load(const char* path) {
         char arch[64];
         int op, xo, wo, f32, id;
         long long M, K, N;
+        float ms = -1.0f;
         if (line[0] == '\n' || line[0] == '#') continue;
-        if (std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d", arch, &op, &M, &K, &N, &xo, &wo, &f32, &id) != 9) {
+        const int n =
+            std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d %f", arch, &op, &M, &K, &N, &xo, &wo, &f32, &id, &ms);
+        if (n != 9 && n != 10) {
             result = FC_E_INVALID;
             break;
         }
@@ -699,6 +727,11 @@ fc_status fc_plans_load(const char* path) {
         if (st != FC_OK) {
             result = st;
             break;
+        }
+        if (n == 10 && id >= 0) {
+            std::lock_guard<std::mutex> lk(g_mu);
+            auto it = g_plans.find(make_key(dev, (fc_op)op, M, K, N, xo, wo, f32));
+            if (it != g_plans.end()) it->second.ms = ms;
         }
     }
     std::fclose(f);

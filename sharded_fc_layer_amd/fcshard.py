@@ -46,6 +46,11 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sharded_fc_layer_amd.build`")
+        # torch carries its own HIP runtime. Loaded first, it also serves this
+        # library's HIP dependency, so torch's memory and streams and this
+        # library's calls live in one runtime; loaded after, the process would
+        # hold two runtimes and this library's calls fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, ci, cs = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         L.fc_fwd.argtypes = [vp, ci, vp, ci, vp, ci, i64, i64, i64, vp]
@@ -173,6 +178,8 @@ def fc_plan_describe(op: int, M: int, K: int, N: int, x_order: int = ROW, w_orde
     d = dict(re.findall(r"(\w+)=(gemm_\w+_kernel<[^>]*>|\S+)", text))
     for k in ("plan", "split", "copy", "ws"):
         d[k] = int(d[k])
+    if "tuned_ms" in d:
+        d["tuned_ms"] = float(d["tuned_ms"])
     return d
 
 

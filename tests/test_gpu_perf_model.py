@@ -1,0 +1,70 @@
+"""The GPU side of the time-per-batch model: fc_tune's measured times reach the
+plan file, and the model's compute term is checked against one GPU running the
+same shard GEMM stream back to back."""
+from __future__ import annotations
+
+import os
+import sys
+
+import pytest
+
+from sharded_fc_layer_amd import fcshard as F
+from sharded_fc_layer_amd import perf_model as PM
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def test_tuned_time_is_kept_saved_and_loaded(tmp_path):
+    F.fc_release()
+    F.fc_tune(512, 256, 384)
+    d = F.fc_plan_describe(F.OP_FWD, 512, 256, 384)
+    assert d["tuned_ms"] > 0
+    p = str(tmp_path / "plans.txt")
+    F.fc_plans_save(p)
+    rows = [l.split() for l in open(p) if l.strip()]
+    assert len(rows) == 3 and all(len(r) == 10 for r in rows)
+    F.fc_release()
+    assert "tuned_ms" not in F.fc_plan_describe(F.OP_FWD, 512, 256, 384)
+    F.fc_plans_load(p)
+    d2 = F.fc_plan_describe(F.OP_FWD, 512, 256, 384)
+    assert d2["plan"] == d["plan"] and abs(d2["tuned_ms"] - d["tuned_ms"]) <= 1e-6
+    # a forced plan carries no time
+    F.fc_set_plan(F.OP_FWD, 512, 256, 384, 0, 0, 0, d["plan"])
+    assert "tuned_ms" not in F.fc_plan_describe(F.OP_FWD, 512, 256, 384)
+    F.fc_release()
+
+
+def test_measure_rank_validate(tmp_path):
+    model = PM.Model("small", 512, 2048, 2, 0, 4096)
+    p = str(tmp_path / "plans.txt")
+    F.fc_release()
+    n = PM.measure(model, 4, p)
+    log(f"tuned {n} shapes")
+    assert n == len(PM.needed_shapes(model, 4))
+    done, missing = PM.rank(model, 4, PM.Machine(), PM.times_from_plan_file(p))
+    assert not missing and len(done) == len(PM.grids(4))
+    r = PM.validate(model, PM.Grid(1, 2, 1, 2), p, steps=10, warmup=3)
+    log(str(r))
+    assert r["gemms"] == 12 and 0.3 < r["predicted_over_measured"] < 3.0
+    F.fc_release()
+
+
+def test_cli_in_a_fresh_process(tmp_path):
+    """The command line loads the library before anything imports torch (the
+    binding must still share torch's HIP runtime)."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = str(tmp_path / "plans.txt")
+    cmd = [sys.executable, "-m", "sharded_fc_layer_amd.perf_model", "measure", "--out", p,
+           "--hidden", "256", "--ffn", "1024", "--layers", "1", "--tokens", "1024", "--gpus", "2"]
+    r = subprocess.run(cmd, cwd=root, capture_output=True, text=True, timeout=180)
+    log(r.stdout[-2000:] + r.stderr[-2000:])
+    assert r.returncode == 0
+    assert PM.times_from_plan_file(p)
