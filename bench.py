@@ -103,13 +103,18 @@ class Layer:
         self.Y = torch.empty((g.M, g.N), dtype=torch.bfloat16, device="cuda")
         self.dX = torch.empty((g.M, g.K), dtype=torch.bfloat16, device="cuda")
         self.dW = torch.empty((g.K, g.N), dtype=torch.bfloat16, device="cuda")
+        self.dW32 = None  # set: dW is added into this fp32 buffer (gradient accumulation)
 
     def calls(self):
         F = self.F
+        if self.dW32 is not None:
+            dw = lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW32, out_dtype=F.OUT_F32_ACC)  # noqa: E731
+        else:
+            dw = lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW)  # noqa: E731
         return [
             ("fwd", F.OP_FWD, lambda: F.fc_fwd(self.X, self.W, out=self.Y)),
             ("bwd_data", F.OP_BWD_DATA, lambda: F.fc_bwd_data(self.dY, self.W, out=self.dX)),
-            ("bwd_weight", F.OP_BWD_WEIGHT, lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW)),
+            ("bwd_weight", F.OP_BWD_WEIGHT, dw),
         ]
 
 
@@ -384,6 +389,23 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         result["large_shard_context"] = extra
+        # the same step with every dW added into an fp32 gradient buffer
+        # (accumulation over micro-batches), for context
+        Ls = make_layers(args.workload, torch, F, I, host_inputs=False)
+        for L in Ls:
+            L.dW32 = torch.zeros((L.g.K, L.g.N), dtype=torch.float32, device="cuda")
+            if not args.no_tune:
+                F.fc_tune(L.g.M, L.g.K, L.g.N)
+                F.fc_tune(L.g.M, L.g.K, L.g.N, out_dtype=F.OUT_F32_ACC)
+        wms, _, _ = run_timed(Ls, 10, 3, torch)
+        wf = step_flops(Ls)
+        result["dw_accumulate_context"] = {
+            "tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
+            "dw_dtype": "fp32, added into (FC_OUT_F32_ACCUMULATE)",
+            "dw_extra_bytes_per_step": int(sum(6 * L.g.K * L.g.N for L in Ls))}
+        log(f"dW accumulate: {result['dw_accumulate_context']}")
+        del Ls
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")

@@ -61,8 +61,13 @@ typedef enum {
 /* storage order of a LOGICAL matrix */
 typedef enum { FC_ROW_MAJOR = 0, FC_COL_MAJOR = 1 } fc_order;
 
-/* output element type */
-typedef enum { FC_OUT_BF16 = 0, FC_OUT_F32 = 1 } fc_out_dtype;
+/*
+ * output element type. FC_OUT_F32_ACCUMULATE: the output is fp32 and already
+ * holds values; the product is added to them (C = C + product, one fp32 add
+ * per element after the product's own fp32 sum), e.g. to accumulate dW over
+ * micro-batches. The output must then be initialised by the caller.
+ */
+typedef enum { FC_OUT_BF16 = 0, FC_OUT_F32 = 1, FC_OUT_F32_ACCUMULATE = 2 } fc_out_dtype;
 
 /* the three products, for the plan-control calls */
 typedef enum { FC_OP_FWD = 0, FC_OP_BWD_DATA = 1, FC_OP_BWD_WEIGHT = 2 } fc_op;

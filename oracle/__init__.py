@@ -140,6 +140,18 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return default().round_bf16(v)
 
 
+def accumulate(C_old: np.ndarray, P: np.ndarray, S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """An accumulating output: the fp32 values it held plus the exact product P.
+
+    Gradient accumulation over micro-batches adds each micro-batch's product to
+    the running fp32 sum (the pages are silent on it; this is its plain
+    definition). Returns (C_old + P, |C_old| + S) in fp64: the value and the
+    magnitude scale that the tolerance applies to.
+    """
+    C = np.asarray(C_old, dtype=np.float64)
+    return C + P, np.abs(C) + S
+
+
 def compare(G: np.ndarray, O: np.ndarray, S: np.ndarray, elem_tol: float = 1e-2,
             fro_tol: float = 5e-3) -> dict:
     """Tolerance check of a GPU result G (any float dtype) against (O, S).

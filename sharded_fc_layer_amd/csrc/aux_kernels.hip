@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_v8_kernel(const uint16_t* 
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ out,
-                                                            bool out_f32, int64_t n, int splits,
+                                                            bool out_f32, bool accumulate, int64_t n, int splits,
                                                             int64_t stride, bool vec) {
     const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i4 >= n) return;
@@ -92,7 +92,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         f32x4 s = *reinterpret_cast<const f32x4*>(ws + i4);
         for (int k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(ws + k * stride + i4);
         if (out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i4) = s;
+            float* o = static_cast<float*>(out) + i4;
+            if (accumulate) s = *reinterpret_cast<const f32x4*>(o) + s;
+            *reinterpret_cast<f32x4*>(o) = s;
         } else {
             typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
             *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + i4) =
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         float s = ws[i];
         for (int k = 1; k < splits; ++k) s += ws[k * stride + i];
         if (out_f32)
-            static_cast<float*>(out)[i] = s;
+            static_cast<float*>(out)[i] = accumulate ? static_cast<float*>(out)[i] + s : s;
         else
             static_cast<__bf16*>(out)[i] = (__bf16)s;
     }
@@ -142,8 +144,8 @@ hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t row
     return hipGetLastError();
 }
 
-hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, int64_t n, int splits, int64_t stride,
-                                hipStream_t stream) {
+hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, bool accumulate, int64_t n, int splits,
+                                int64_t stride, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int64_t threads = (n + 3) / 4;
     const int64_t blocks = (threads + 255) / 256;
@@ -151,8 +153,8 @@ hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, int64_
     // vector path: 16-byte partial loads and 8/16-byte output stores
     const bool vec = (stride % 4 == 0) && ((uintptr_t)ws % 16 == 0) &&
                      ((uintptr_t)out % (out_f32 ? 16 : 8) == 0);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, out, out_f32, n,
-                       splits, stride, vec);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, out, out_f32,
+                       out_f32 && accumulate, n, splits, stride, vec);
     return hipGetLastError();
 }
 

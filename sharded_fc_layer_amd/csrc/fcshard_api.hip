@@ -73,6 +73,7 @@ struct Problem {
     const uint16_t* B;
     void* C;
     bool a_oc, b_oc, out_f32;
+    bool accumulate;  // fp32 output: C += product
     int64_t M, N, K;  // output rows, output cols, reduction
 };
 
@@ -272,7 +273,8 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
     g.ldb = ldb;
     g.k_split = ks;
     g.splits = slices;
-    if (slices > 1) {
+    g.accumulate = 0;
+    if (slices > 1) {  // partial planes, summed (and added to C) by the reduction
         float* part = reinterpret_cast<float*>(base + w.p_off);
         g.C = part;
         g.c_split_stride = p.M * p.N;
@@ -281,10 +283,11 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
             : pl.family >= 2          ? launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, true, g, s)
                              : launch_gemm(pl.tile, p.a_oc, p.b_oc, true, aligned, g, s);
         if (e != hipSuccess) return e;
-        return launch_splitk_reduce(part, p.C, p.out_f32, p.M * p.N, slices, p.M * p.N, s);
+        return launch_splitk_reduce(part, p.C, p.out_f32, p.accumulate, p.M * p.N, slices, p.M * p.N, s);
     }
     g.C = p.C;
     g.c_split_stride = 0;
+    g.accumulate = p.accumulate ? 1 : 0;
     if (pl.family == 0) return launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= kFamilyW4) return launch_gemm_w4(pl.family - kFamilyW4, p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= 2) return launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, p.out_f32, g, s);
@@ -294,7 +297,7 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
 // ------------------------------------------------------------ validation
 
 bool bad_order(int o) { return o != FC_ROW_MAJOR && o != FC_COL_MAJOR; }
-bool bad_dtype(int d) { return d != FC_OUT_BF16 && d != FC_OUT_F32; }
+bool bad_dtype(int d) { return d != FC_OUT_BF16 && d != FC_OUT_F32 && d != FC_OUT_F32_ACCUMULATE; }
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)abytes;
@@ -310,7 +313,8 @@ fc_status resolve(int op, const void* P, int p_order, const void* Q, int q_order
     if (bad_order(p_order) || bad_order(q_order) || bad_dtype(dtype)) return FC_E_INVALID;
     if (M > (int64_t)1 << 31 || K > (int64_t)1 << 31 || N > (int64_t)1 << 31) return FC_E_INVALID;
     Problem p;
-    p.out_f32 = dtype == FC_OUT_F32;
+    p.out_f32 = dtype != FC_OUT_BF16;
+    p.accumulate = dtype == FC_OUT_F32_ACCUMULATE;
     p.A = static_cast<const uint16_t*>(P);
     p.B = static_cast<const uint16_t*>(Q);
     p.C = out;
@@ -574,7 +578,7 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
     }
     (void)hipGetLastError();  // as in hot_call: no stale error from an earlier HIP call
     TuneBuffers b;
-    const int64_t esz = out_dtype == FC_OUT_F32 ? 4 : 2;
+    const int64_t esz = out_dtype == FC_OUT_BF16 ? 2 : 4;
     const int64_t out_elems = std::max(M * N, std::max(M * K, K * N));
     if (hipMalloc(&b.X, M * K * 2) != hipSuccess || hipMalloc(&b.W, K * N * 2) != hipSuccess ||
         hipMalloc(&b.dY, M * N * 2) != hipSuccess || hipMalloc(&b.out, out_elems * esz) != hipSuccess) {
@@ -584,6 +588,8 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
     hipError_t fe = launch_fill_bf16((uint16_t*)b.X, M * K, 1u, s);
     if (fe == hipSuccess) fe = launch_fill_bf16((uint16_t*)b.W, K * N, 2u, s);
     if (fe == hipSuccess) fe = launch_fill_bf16((uint16_t*)b.dY, M * N, 3u, s);
+    // an accumulating output starts from zeros (the timed calls add into it)
+    if (fe == hipSuccess && out_dtype == FC_OUT_F32_ACCUMULATE) fe = hipMemsetAsync(b.out, 0, out_elems * esz, s);
     if (fe != hipSuccess) {
         if (log_enabled()) std::fprintf(stderr, "[fcshard] tune: filling the operands failed: %s\n", hipGetErrorString(fe));
         return FC_E_HIP;

@@ -23,6 +23,7 @@ struct GemmArgs {
     int64_t k_split;         // reduction elements per split slice (multiple of 64)
     int splits;              // number of reduction slices; 1 = no split
     int64_t c_split_stride;  // elements between the slices' fp32 partial outputs
+    int accumulate;          // 1: fp32 C += product (one slice only); 0: C = product
 };
 
 struct TileCfg {
@@ -72,8 +73,9 @@ const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                  hipStream_t stream);
 
-// out[i] = sum_{s < splits} ws[s * stride + i] (fixed order), stored bf16 or fp32.
-hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, int64_t n, int splits,
+// out[i] = sum_{s < splits} ws[s * stride + i] (fixed order), stored bf16 or
+// fp32; with `accumulate` (fp32 only) out[i] = out[i] + that sum.
+hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, bool accumulate, int64_t n, int splits,
                                 int64_t stride, hipStream_t stream);
 
 // Deterministic pseudo-random bf16 fill in [-1, 1) (tuning buffers only).

@@ -261,12 +261,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g) {
                 if (OUT_F32) {
                     float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * ldc + n;
                     if (ALIGNED) {
-                        if (n < g.N) *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+                        if (n < g.N) {
+                            f32x4 v{v0, v1, v2, v3};
+                            if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
+                            *reinterpret_cast<f32x4*>(c) = v;
+                        }
                     } else {
-                        if (n + 0 < g.N) c[0] = v0;
-                        if (n + 1 < g.N) c[1] = v1;
-                        if (n + 2 < g.N) c[2] = v2;
-                        if (n + 3 < g.N) c[3] = v3;
+                        const float vs[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < g.N) c[q] = g.accumulate ? c[q] + vs[q] : vs[q];
                     }
                 } else {
                     __bf16* c = static_cast<__bf16*>(g.C) + m * ldc + n;

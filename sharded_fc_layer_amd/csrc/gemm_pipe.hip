@@ -162,7 +162,9 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
                 const float v2 = acc[i][j][grp * 4 + 2], v3 = acc[i][j][grp * 4 + 3];
                 if (OUT_F32) {
                     float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
-                    *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
+                    f32x4 v{v0, v1, v2, v3};
+                    if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
+                    *reinterpret_cast<f32x4*>(c) = v;
                 } else {
                     __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
                     *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libfcshard.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fcshard.h")
 
 ROW, COL = 0, 1                # fc_order
-OUT_BF16, OUT_F32 = 0, 1       # fc_out_dtype
+OUT_BF16, OUT_F32, OUT_F32_ACC = 0, 1, 2  # fc_out_dtype (OUT_F32_ACC: fp32 out += product)
 OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2  # fc_op
 FC_OK, FC_E_INVALID, FC_E_UNSUPPORTED, FC_E_HIP, FC_E_NOMEM = 0, 1, 2, 3, 4
 
@@ -105,8 +105,10 @@ def _logical(t, order: int):
 
 def _out(out, rows: int, cols: int, out_dtype: int, like, name: str):
     import torch
-    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
     if out is None:
+        if out_dtype == OUT_F32_ACC:
+            raise ValueError(f"{name}: accumulating needs the existing output tensor (out=)")
         return torch.empty((rows, cols), dtype=dt, device=like.device)
     if out.dtype != dt or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {(rows, cols)}")

@@ -43,6 +43,7 @@ def test_enum_values_match_header():
     for name, val in [("FC_OK", F.FC_OK), ("FC_E_INVALID", F.FC_E_INVALID), ("FC_E_UNSUPPORTED", F.FC_E_UNSUPPORTED),
                       ("FC_E_HIP", F.FC_E_HIP), ("FC_E_NOMEM", F.FC_E_NOMEM), ("FC_ROW_MAJOR", F.ROW),
                       ("FC_COL_MAJOR", F.COL), ("FC_OUT_BF16", F.OUT_BF16), ("FC_OUT_F32", F.OUT_F32),
+                      ("FC_OUT_F32_ACCUMULATE", F.OUT_F32_ACC),
                       ("FC_OP_FWD", F.OP_FWD), ("FC_OP_BWD_DATA", F.OP_BWD_DATA),
                       ("FC_OP_BWD_WEIGHT", F.OP_BWD_WEIGHT)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
@@ -70,6 +71,8 @@ def test_null_and_bad_dimensions_rejected_without_a_device(L):
     # misaligned and overlapping outputs
     assert L.fc_fwd(a, 0, b, 0, ctypes.c_void_p(0x300001), 0, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_fwd(a, 0, b, 0, ctypes.c_void_p(0x300002), 1, 8, 8, 8, None) == F.FC_E_INVALID
+    assert L.fc_fwd(a, 0, b, 0, ctypes.c_void_p(0x300002), 2, 8, 8, 8, None) == F.FC_E_INVALID  # fp32 alignment
+    assert L.fc_fwd(a, 0, b, 0, c, 3, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_fwd(a, 0, b, 0, ctypes.c_void_p(0x100010), 0, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_tune(0, 8, 8, 0, 0, 0, 0, None) == F.FC_E_INVALID
     assert L.fc_set_plan(0, 8, 8, 8, 0, 0, 0, 432) == F.FC_E_INVALID

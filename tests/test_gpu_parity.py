@@ -172,6 +172,86 @@ def test_exact_integer_every_plan(shape):
                 F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, -1)
 
 
+# ------------------------------------------------ accumulating fp32 output
+
+def _out_shape(op, M, K, N):
+    return {"fwd": (M, N), "bwd_data": (M, K), "bwd_weight": (K, N)}[op]
+
+
+def gpu_acc(c: Case, op: str, C_old: np.ndarray):
+    """The product added into a device copy of C_old (fp32)."""
+    out = torch.from_numpy(np.ascontiguousarray(C_old, dtype=np.float32)).to("cuda")
+    acc = F.OUT_F32_ACC
+    if op == "fwd":
+        F.fc_fwd(c.X, c.W, c.xo, c.wo, out=out, out_dtype=acc)
+    elif op == "bwd_data":
+        F.fc_bwd_data(c.dY, c.W, c.wo, out=out, out_dtype=acc)
+    else:
+        F.fc_bwd_weight(c.X, c.dY, c.xo, out=out, out_dtype=acc)
+    return out
+
+
+@pytest.mark.parametrize("shape", [(264, 520, 136), (384, 1024, 384)], ids=lambda s: "x".join(map(str, s)))
+def test_accumulate_exact_every_plan(shape):
+    """Every plan, split-K ones included, adds the exact product to the old values."""
+    M, K, N = shape
+    d = I.make_integer_inputs(M, K, N, seed=8)
+    rng = np.random.default_rng(8)
+    acc = F.OUT_F32_ACC
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        for op in OPS:
+            O, S = c.oracle(op)
+            C_old = rng.integers(-64, 65, size=_out_shape(op, M, K, N)).astype(np.float32)
+            want, _ = oracle.accumulate(C_old, O, S)
+            ran = 0
+            for pid in range(F.fc_plan_count()):
+                st = F.fc_set_plan(op_code(op), M, K, N, xo, wo, acc, pid)
+                if st == F.FC_E_UNSUPPORTED:
+                    continue
+                assert st == F.FC_OK, F.status_str(st)
+                desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, acc)
+                what = f"acc {op} {shape} orders={xo}{wo} plan={pid} {desc['kernel']} split={desc['split']}"
+                log(what)
+                G = host(gpu_acc(c, op, C_old))
+                assert_exact(G, want, F.OUT_F32, what)
+                ran += 1
+            assert ran >= 1
+            F.fc_set_plan(op_code(op), M, K, N, xo, wo, acc, -1)
+
+
+@pytest.mark.parametrize("shape", [(777, 1000, 555), (513, 2056, 257), (1024, 2048, 1536)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_accumulate_tolerance_tuned(shape):
+    M, K, N = shape
+    d = I.make_random_inputs(M, K, N, seed=9)
+    rng = np.random.default_rng(9)
+    F.fc_tune(M, K, N, ROW, ROW, F.OUT_F32_ACC)
+    c = Case(d, ROW, ROW)
+    for op in OPS:
+        O, S = c.oracle(op)
+        C_old = (rng.standard_normal(_out_shape(op, M, K, N)) * float(np.median(S))).astype(np.float32)
+        want, S2 = oracle.accumulate(C_old, O, S)
+        desc = F.fc_plan_describe(op_code(op), M, K, N, ROW, ROW, F.OUT_F32_ACC)
+        assert_close(host(gpu_acc(c, op, C_old)), want, S2, F.OUT_F32,
+                     f"acc {op} {shape} {desc['kernel']} split={desc['split']}")
+
+
+def test_accumulated_micro_batches_equal_the_whole_batch():
+    """dW accumulated over micro-batches of tokens = dW of the whole batch."""
+    M, K, N = 2048, 1024, 768
+    d = I.make_random_inputs(M, K, N, seed=10)
+    O, S = Case(d, ROW, ROW).oracle("bwd_weight")
+    dW = torch.zeros((K, N), dtype=torch.float32, device="cuda")
+    for lo, hi in ((0, 768), (768, 2048)):
+        part = {"X": np.ascontiguousarray(d["X"][lo:hi]), "W": d["W"], "dY": np.ascontiguousarray(d["dY"][lo:hi])}
+        c = Case(part, ROW, ROW)
+        F.fc_bwd_weight(c.X, c.dY, ROW, out=dW, out_dtype=F.OUT_F32_ACC)
+    assert_close(host(dW), O, S, F.OUT_F32, "two micro-batches vs the whole batch")
+    with pytest.raises(ValueError, match="existing output"):
+        F.fc_bwd_weight(c.X, c.dY, ROW, out_dtype=F.OUT_F32_ACC)
+
+
 # --------------------------------------------------------- tolerance parity
 
 @pytest.mark.parametrize("dt", [F.OUT_BF16, F.OUT_F32])

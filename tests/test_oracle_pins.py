@@ -363,6 +363,48 @@ def test_grid_single_axis_and_uneven(g):
     _grid_vs_full(I.make_random_inputs(11, 10, 13, seed=2), g, exact=False)
 
 
+# ------------------------------------------ accumulating output (micro-batches)
+
+def _micro_batches(d, cuts, orc):
+    M, K = d["X"].shape
+    N = d["dY"].shape[1]
+    C = np.zeros((K, N), dtype=np.float32)
+    S = np.zeros((K, N))
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        X1, dY1 = np.ascontiguousarray(d["X"][lo:hi]), np.ascontiguousarray(d["dY"][lo:hi])
+        P, S1 = orc.fc_bwd_weight(X1, ROW, dY1, hi - lo, K, N)
+        V, S = oracle.accumulate(C, P, S1)
+        C = V.astype(np.float32)
+    return V, S
+
+
+def test_accumulated_micro_batches_equal_the_whole_batch():
+    # dW = X^T dY sums over tokens, so adding the micro-batches' products into
+    # one output gives the whole batch's product (exact on integer data)
+    orc = oracle.default()
+    d = I.make_integer_inputs(24, 10, 7, seed=5)
+    full, S_full = run_oracle(orc, "bwd_weight", d, ROW, ROW)
+    V, S = _micro_batches(d, [0, 9, 16, 24], orc)
+    assert np.array_equal(V, full)
+    assert np.all(S <= S_full)  # |partial sums| never exceed the sums of |terms|
+    d = I.make_random_inputs(40, 12, 9, seed=6)
+    full, S_full = run_oracle(orc, "bwd_weight", d, ROW, ROW)
+    V, _ = _micro_batches(d, [0, 13, 40], orc)
+    # fp32 storage of the running sum between micro-batches: half an ulp of fp32
+    assert np.all(np.abs(V - full) <= 2.0 ** -23 * S_full + 1e-12 * S_full)
+
+
+def test_accumulate_identities():
+    rng = np.random.default_rng(0)
+    C = rng.standard_normal((5, 6)).astype(np.float32)
+    P = rng.standard_normal((5, 6))
+    S = np.abs(P) + 1.0
+    V, S2 = oracle.accumulate(C, np.zeros_like(P), np.zeros_like(S))
+    assert np.array_equal(V, C.astype(np.float64)) and np.array_equal(S2, np.abs(C).astype(np.float64))
+    V, S2 = oracle.accumulate(np.zeros((5, 6), dtype=np.float32), P, S)
+    assert np.array_equal(V, P) and np.array_equal(S2, S)
+
+
 # ------------------------------------------------------------- bf16 rounding
 
 def _nearest_even_bf16(v: float) -> int:
