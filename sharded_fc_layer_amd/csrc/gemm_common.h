@@ -42,9 +42,16 @@ __device__ __forceinline__ uint32_t rc_slot_k(int i, int c) {
     return i * (BKP * 2) + ((c ^ rc_swizzle<BKP>(i)) << 4);
 }
 
+// Output-contiguous tile row k (R values): 16-byte chunk c XOR (k & 3) << 2,
+// and bit 1 of the XOR from bit 3 of k. A half-wave ds_read_b64_tr_b16 of a
+// 16x16x32 operand reads rows k0 .. k0+3 and k0+8 .. k0+11 (32 B each); with
+// bit 3 folded in, those 8 rows fall on 8 different 32-byte bank groups
+// (conflict-free; with (k & 3) << 2 alone, rows k and k + 8 shared banks).
+// The 32x32x16 operand reads 4 rows x 64 B per half-wave, conflict-free either way.
+__device__ __forceinline__ int oc_swizzle(int k) { return ((k & 3) << 2) | ((k & 8) >> 2); }
 template <int R>
 __device__ __forceinline__ uint32_t oc_slot(int k, int c) {
-    return k * (R * 2) + ((c ^ ((k & 3) << 2)) << 4);
+    return k * (R * 2) + ((c ^ oc_swizzle(k)) << 4);
 }
 
 // s_waitcnt with vmcnt = vm, lgkmcnt = lgkm (expcnt not waited)
@@ -73,7 +80,7 @@ struct Dma {
                 constexpr int CPR = R / 8;     // 16-byte chunks per reduction row
                 constexpr int RPI = 64 / CPR;  // reduction rows per instruction
                 const int k = (wave * kInstr + j) * RPI + lane / CPR;
-                const int c = (lane % CPR) ^ ((k & 3) << 2);
+                const int c = (lane % CPR) ^ oc_swizzle(k);
                 kk[j] = k;
                 base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
             }
@@ -137,7 +144,7 @@ struct DmaPP {
             } else {
                 constexpr int CPR = R / 8;
                 const int k = p / CPR;
-                const int c = (p % CPR) ^ ((k & 3) << 2);
+                const int c = (p % CPR) ^ oc_swizzle(k);
                 kk[j] = k;
                 base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
             }

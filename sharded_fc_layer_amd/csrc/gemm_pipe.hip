@@ -17,7 +17,7 @@
 //    16-byte chunk index XOR-swizzled with (row >> 2) & 3; MFMA operands are
 //    single ds_read_b128.
 //  * Output-contiguous operands are stored untransposed (LDS row = one
-//    reduction index, chunk index XOR-swizzled with (k & 3) << 2) and read
+//    reduction index, chunk index XOR-swizzled by oc_swizzle(k)) and read
 //    with ds_read_b64_tr_b16: within each 16-lane group, lane j addresses
 //    reduction row k0 + j / 4 at columns base + 4 (j % 4), and lane i
 //    receives the four reduction values k0 .. k0+3 of column base + i. Two
