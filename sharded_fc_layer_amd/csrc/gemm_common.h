@@ -278,6 +278,40 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t
     }
 }
 
+// bf16 epilogue of a 128 x 128 wave tile of 16 x 16 blocks (acc[i][j]: lane
+// holds row 16 i + lane % 16, columns 16 j + 4 (lane / 16) .. +3), staged
+// through `stage`, 32 KB of LDS that this wave alone uses. Written straight
+// from the registers, each store instruction would cover 16 rows x 32 B
+// (quarter cache lines); staged, the wave writes its 8-byte pieces into LDS
+// rows of 256 B and reads back 16-byte chunks, so each store writes 4 rows x
+// 256 B of whole 128-byte lines, with half as many store instructions. The
+// 16-byte chunk index in an LDS row is XOR-swizzled by the row (mod 16):
+// a half-wave's writes (16 rows x 16 B) and a row's reads (16 chunks) then
+// fall on distinct banks. Needs N % 8 == 0 and a 16-byte-aligned C.
+__device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_t m0, int64_t n0, int wm0, int wn0,
+                                                       int lane, const f32x4 (&acc)[8][8], char* stage) {
+    const int lr = lane & 15, lk = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = i * 16 + lr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = j * 16 + lk * 4;
+            const uint32_t off = row * 256 + (((col >> 3) ^ (row & 15)) << 4) + ((col & 7) << 1);
+            const f32x4 v = acc[i][j];
+            *reinterpret_cast<bf16x4*>(stage + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        }
+    }
+    const int rq = lane >> 4, ch = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        const int row = q * 4 + rq;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
+        const int64_t m = m0 + wm0 + row, n = n0 + wn0 + ch * 8;
+        if (m < g.M && n < g.N) *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.N + n) = v;
+    }
+}
+
 // Output tile and reduction slice of this block. Blocks are dealt round robin
 // to the 8 XCDs; the map gives each XCD one contiguous range of tile ids, and
 // walks tiles in groups of kGroupM tile-rows so that the blocks resident on
