@@ -312,6 +312,43 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
     }
 }
 
+// fp32 epilogue of the same wave tile (fp32 and accumulating outputs,
+// split-K partial planes), staged the same way in two passes of 64 rows:
+// LDS rows of 512 B with the 16-byte chunk XOR-swizzled by (row & 7) << 1,
+// which spreads both a half-wave's writes and a row's reads evenly over the
+// banks. Each store writes 2 rows x 512 B of whole lines; an accumulating
+// output is read back the same way and added. Within one wave, LDS accesses
+// complete in order, so the second pass may overwrite what the first read.
+__device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int slice, int64_t m0, int64_t n0, int wm0,
+                                                      int wn0, int lane, const f32x4 (&acc)[8][8], char* stage) {
+    const int lr = lane & 15, lk = lane >> 4;
+    float* C = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i * 16 + lr;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int ch = 4 * j + lk;
+                *reinterpret_cast<f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
+            }
+        }
+        const int rq = lane >> 5, ch = lane & 31;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int row = 2 * q + rq;
+            f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
+            const int64_t m = m0 + wm0 + 64 * h + row, n = n0 + wn0 + 4 * ch;
+            if (m < g.M && n < g.N) {
+                float* c = C + m * g.N + n;
+                if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
+                *reinterpret_cast<f32x4*>(c) = v;
+            }
+        }
+    }
+}
+
 // Output tile and reduction slice of this block. Blocks are dealt round robin
 // to the 8 XCDs; the map gives each XCD one contiguous range of tile ids, and
 // walks tiles in groups of kGroupM tile-rows so that the blocks resident on

@@ -166,15 +166,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCW4_READ
 #undef FCW4_STAGE
 
-    if constexpr (OUT_F32) {
-        store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
-    } else {
-        // the tiles become staging space: every wave's loads must have landed
-        // and its LDS reads finished before any wave writes there
-        waitcnt<0, 0>();
-        __builtin_amdgcn_s_barrier();
+    // the tiles become staging space: every wave's loads must have landed
+    // and its LDS reads finished before any wave writes there
+    waitcnt<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (OUT_F32)
+        store_tile_f32_staged(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc, smem + wave * (128 * 256));
+    else
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, smem + wave * (128 * 256));
-    }
 }
 
 // Placement of a 64-MFMA step's 16 fragment reads and NL loads: the index of
@@ -346,15 +345,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCW64_STAGE
     w4_acc_drain(acc);  // the last MFMAs must have written their results before the epilogue reads them
 
-    if constexpr (OUT_F32) {
-        store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
-    } else {
-        // the tiles become staging space: every wave's loads must have landed
-        // and its LDS reads finished before any wave writes there
-        waitcnt<0, 0>();
-        __builtin_amdgcn_s_barrier();
+    // the tiles become staging space: every wave's loads must have landed
+    // and its LDS reads finished before any wave writes there
+    waitcnt<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (OUT_F32)
+        store_tile_f32_staged(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc, wave == 0 ? a0 : wave == 1 ? b0 : wave == 2 ? a1 : b1);
+    else
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, wave == 0 ? a0 : wave == 1 ? b0 : wave == 2 ? a1 : b1);
-    }
 }
 // gemm_w4k64r_kernel: the 64-value stages of gemm_w4k64_kernel in the whole
 // 160 KB LDS, as a ring of three A tiles and two B tiles (32 KB each, one
@@ -478,15 +476,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCR_STAGE
     w4_acc_drain(acc);  // the last MFMAs must have written their results before the epilogue reads them
 
-    if constexpr (OUT_F32) {
-        store_tile<MF, 8, 8, OUT_F32>(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc);
-    } else {
-        // the tiles become staging space: every wave's loads must have landed
-        // and its LDS reads finished before any wave writes there
-        waitcnt<0, 0>();
-        __builtin_amdgcn_s_barrier();
+    // the tiles become staging space: every wave's loads must have landed
+    // and its LDS reads finished before any wave writes there
+    waitcnt<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (OUT_F32)
+        store_tile_f32_staged(g, w.slice, w.m0, w.n0, wm0, wn0, lane, acc, wave == 0 ? ta0 : wave == 1 ? ta1 : wave == 2 ? ta2 : tb0);
+    else
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, wave == 0 ? ta0 : wave == 1 ? ta1 : wave == 2 ? ta2 : tb0);
-    }
 }
 #undef FCW4_MFMA_STEP
 
