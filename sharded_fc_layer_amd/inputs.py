@@ -133,6 +133,24 @@ def normal_bf16_chunked(key: Sequence[int], shape: Tuple[int, int], std: float) 
     return out.reshape(shape)
 
 
+def integer_bf16_chunked(key: Sequence[int], shape: Tuple[int, int], lo: int = -3, hi: int = 3) -> np.ndarray:
+    """Integers uniform in [lo, hi] as bf16 bits (exact), for arrays too large for
+    integer_bf16; chunk j of the flat array comes from default_rng(key + [j])."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+
+    def work(j: int) -> None:
+        a = j * CHUNK
+        b = min(n, a + CHUNK)
+        x = np.random.default_rng(list(key) + [j]).integers(lo, hi + 1, size=b - a, dtype=np.int8)
+        out[a:b] = f32_to_bf16_bits(x.astype(np.float32))
+
+    nchunks = (n + CHUNK - 1) // CHUNK
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(nchunks)))
+    return out.reshape(shape)
+
+
 def normal_bf16(rng: np.random.Generator, shape: Tuple[int, ...], std: float) -> np.ndarray:
     """float32 N(0, std) draws rounded to bf16 (std is a standard deviation)."""
     x = rng.standard_normal(shape, dtype=np.float32)

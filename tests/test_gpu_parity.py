@@ -252,6 +252,35 @@ def test_accumulated_micro_batches_equal_the_whole_batch():
         F.fc_bwd_weight(c.X, c.dY, ROW, out_dtype=F.OUT_F32_ACC)
 
 
+# ------------------------------------------------------------ maximum sizes
+
+def test_operands_of_2_gib_and_more():
+    """X of 2 GiB and more is past the fast kernels' buffer descriptors: those
+    plans do not apply and the simple kernel (64-bit addressing) runs the
+    products that read X; backward-data writes a dX of 2 GiB and more.
+    Integer-valued data, exact on sampled outputs."""
+    M, K, N = 131080, 8192, 264  # X: 2.0002 GiB
+    log(f"generating {M}x{K} integer inputs")
+    d = {"X": I.integer_bf16_chunked([31, 1], (M, K)), "W": I.integer_bf16_chunked([31, 2], (K, N)),
+         "dY": I.integer_bf16_chunked([31, 3], (M, N))}
+    c = Case(d, ROW, ROW)
+    rng = np.random.default_rng(31)
+    for op in OPS:
+        desc = F.fc_plan_describe(op_code(op), M, K, N)
+        what = f"max-size {op} {desc['kernel']}"
+        log(what)
+        if op != "bwd_data":
+            assert desc["kernel"].startswith("gemm_bf16_kernel"), what
+        Gt = c.gpu(op, F.OUT_BF16)
+        rows, cols = _sample(Gt.shape[0], 24, rng), _sample(Gt.shape[1], 96, rng)
+        O, _ = c.oracle(op, rows, cols)
+        G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+        assert_exact(G, O, F.OUT_BF16, what)
+        del Gt
+    del c
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------- tolerance parity
 
 @pytest.mark.parametrize("dt", [F.OUT_BF16, F.OUT_F32])
