@@ -142,8 +142,10 @@ def test_exact_power_of_two_scaled_inputs():
 # so the kernels that take 32-value reduction stages in pairs run too, with
 # ragged output tiles and two- and four-way reduction splits. (384, 1024, 384):
 # every reduction a multiple of 128 (64-value stages in pairs), ragged tiles.
+# (352, 608, 224): every reduction length is 32 more than a multiple of 64;
+# split slices of 320 + 288 and of 192 + 192 + 192 + 32.
 @pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192),
-                                   (384, 1024, 384)],
+                                   (384, 1024, 384), (352, 608, 224)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
@@ -191,7 +193,8 @@ def gpu_acc(c: Case, op: str, C_old: np.ndarray):
     return out
 
 
-@pytest.mark.parametrize("shape", [(264, 520, 136), (384, 1024, 384)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(264, 520, 136), (384, 1024, 384), (352, 608, 224)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_accumulate_exact_every_plan(shape):
     """Every plan, split-K ones included, adds the exact product to the old values."""
     M, K, N = shape
