@@ -16,8 +16,12 @@ message and measures, for one GEMM:
   serialise, below 0 when running them together is slower than one after the
   other.
 
-Each timing is the median of `reps` runs, the three configurations taken in
-turn, with the L2s and the MALL flushed before each run (the GEMM's operands
+With CU masks (copy_cus > 0), the copy's stream runs on a few compute units
+spread over the chip and the GEMM's stream on the others, the way a runtime
+can reserve compute units for communication; the GEMM alone on every compute
+unit is timed beside it.
+
+Each timing is the median of `reps` runs, the configurations taken in turn, with the L2s and the MALL flushed before each run (the GEMM's operands
 come from HBM, as in a training step). The
 GEMM's output under the copy must equal its output alone, bit for bit.
 
@@ -61,17 +65,52 @@ class _Bufs:
             F.fc_bwd_weight(self.X, self.dY, out=self.dW, stream=s)
 
 
+def _hip_runtime():
+    """ctypes handle of the HIP runtime this process already uses (torch's):
+    loading another copy would start a second runtime."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("no HIP runtime is loaded")
+
+
+def cu_masked_stream(torch, cus: Sequence[int]):
+    """A stream (default priority) whose kernels run only on compute units `cus`."""
+    import ctypes
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for c in cus:
+        mask[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = _hip_runtime().hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask returned {rc}")
+    return torch.cuda.ExternalStream(h.value)
+
+
 def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps: int = 7,
-            tune: bool = True) -> List[Dict]:
-    """One record per message size (see the module docstring)."""
+            tune: bool = True, copy_cus: int = 0) -> List[Dict]:
+    """One record per message size (see the module docstring). With copy_cus > 0
+    the copy's stream runs on that many compute units, spread over the chip,
+    and the GEMM's stream on the others (CU-masked streams)."""
     import torch
     if op not in OPS:
         raise ValueError(f"op must be one of {sorted(OPS)}")
     if tune:
         F.fc_tune(M, K, N)
     plan = F.fc_plan_describe(OPS[op], M, K, N)
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()  # default priority
+    if copy_cus > 0:
+        n = torch.cuda.get_device_properties(0).multi_processor_count
+        copy_set = sorted({(i * 33) % n for i in range(copy_cus)})  # 33 is coprime with the CU count
+        main = cu_masked_stream(torch, [c for c in range(n) if c not in copy_set])
+        side = cu_masked_stream(torch, copy_set)
+    else:
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()  # default priority
+    full = torch.cuda.current_stream()
     out = []
     for mb in copy_mbytes:
         b = _Bufs(torch, M, K, N, int(mb * 1e6))
@@ -81,7 +120,7 @@ def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps:
             b.flush_b.copy_(b.flush_a)
             torch.cuda.synchronize()
 
-        def run(gemm: bool, copy: bool):
+        def run(gemm: bool, copy: bool, main=main):
             flush()
             ev[0].record(main)
             side.wait_event(ev[0])
@@ -106,9 +145,11 @@ def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps:
         run(True, False)
         ref = res.clone()  # written with no copy running
         # the three configurations interleaved, so that clock drift hits them alike
-        alone, copy_alone, both = [], [], []
+        alone, copy_alone, both, whole = [], [], [], []
         for _ in range(reps):
             alone.append(run(True, False))
+            if copy_cus > 0:
+                whole.append(run(True, False, main=full))  # the GEMM on every compute unit
             copy_alone.append(run(False, True))
             both.append(run(True, True))
         # the output of the last run, written while the copy ran
@@ -122,7 +163,8 @@ def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps:
                     "gemm_ms": round(t_g, 4), "copy_ms": round(t_c, 4),
                     "copy_GBs": round(2 * mb * 1e6 / (t_c * 1e-3) / 1e9, 1),
                     "gemm_under_copy_ms": round(t_g_under, 4), "copy_under_gemm_ms": round(t_c_under, 4),
-                    "both_ms": round(t_both, 4), "added_ms": round(t_both - t_g, 4),
+                    "both_ms": round(t_both, 4), "added_ms": round(t_both - t_g, 4), "copy_cus": copy_cus,
+                    "gemm_all_cus_ms": round(statistics.median(x[0] for x in whole), 4) if whole else None,
                     "gemm_slowdown": round(t_g_under / t_g, 4),
                     "hidden_fraction": round((t_g + t_c - t_both) / t_c, 4), "output_identical": same})
         del b
@@ -136,9 +178,11 @@ def main(argv=None) -> int:
     ap.add_argument("--op", default="fwd", choices=sorted(OPS))
     ap.add_argument("--mbytes", default="101,151,403", help="message sizes in MB")
     ap.add_argument("--reps", type=int, default=15)
+    ap.add_argument("--copy-cus", type=int, default=0,
+                    help="run the copy on this many compute units and the GEMM on the rest (0: no masks)")
     a = ap.parse_args(argv)
     M, K, N = (int(v) for v in a.shape.split(","))
-    for r in measure(M, K, N, a.op, [float(v) for v in a.mbytes.split(",")], a.reps):
+    for r in measure(M, K, N, a.op, [float(v) for v in a.mbytes.split(",")], a.reps, copy_cus=a.copy_cus):
         print(json.dumps(r), flush=True)
     return 0
 

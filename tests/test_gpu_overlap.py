@@ -23,3 +23,11 @@ def test_gemm_under_a_concurrent_copy(op):
         # both together take at least as long as the longer of the two, within noise
         assert r["both_ms"] >= 0.8 * max(r["gemm_ms"], r["copy_ms"])
         assert r["hidden_fraction"] <= 1.2
+
+
+def test_gemm_beside_a_copy_on_reserved_compute_units():
+    from sharded_fc_layer_amd import overlap as O
+    for r in O.measure(1024, 2048, 1536, "fwd", [16.0], reps=3, copy_cus=8):
+        print(r, file=sys.stderr, flush=True)
+        assert r["output_identical"] and r["copy_cus"] == 8
+        assert r["gemm_all_cus_ms"] > 0 and r["both_ms"] >= 0.8 * max(r["gemm_ms"], r["copy_ms"])
