@@ -83,7 +83,8 @@ def parse():
     p.add_argument("--no-tune", action="store_true", help="use the default plans")
     p.add_argument("--plans", default=None,
                    help="plan file: loaded if it exists (no tuning in this run), else written after tuning")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="CPU oracle timing: the sample doubles until one pass takes at least half of this")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device copy (a known-size reference for HBM counters)")
     return p.parse_args()
