@@ -5,12 +5,15 @@ Reads a rocprofv3 rocpd database (<name>_results.db) and prints, per kernel
 minimum, maximum and total duration; for counter runs (--pmc) it prints the
 per-dispatch averages of each counter. With --traffic it combines a
 FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per launch of each kernel,
-scaled by what the same counters read for a plain copy of known size.
+scaled by what the same counters read for a plain copy of known size. With
+--mfma it turns a run with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE into
+each kernel's engine clock and MFMA busy fraction.
 Usage:
 
   python -m sharded_fc_layer_amd.rocprof_summary RESULTS.db [--by-grid] [--pmc]
   python -m sharded_fc_layer_amd.rocprof_summary --traffic FETCH.db WRITE.db \
       --copy-kernel REGEX --copy-bytes N [--json OUT --workload NAME --source-hash H]
+  python -m sharded_fc_layer_amd.rocprof_summary --mfma MFMA.db
 """
 from __future__ import annotations
 
@@ -79,6 +82,42 @@ def counter_per_dispatch(db: str, counter: str):
     return {k: list(v.values()) for k, v in per.items()}
 
 
+# MI355X: 8 XCDs (one GRBM each), 256 CUs x 4 SIMDs; dense bf16 peak 2.5 PFLOP/s at 2.4 GHz
+XCDS, SIMDS, PEAK_TFLOPS, PEAK_GHZ = 8, 1024, 2500.0, 2.4
+
+
+def mfma_util(db: str, out=sys.stdout):
+    """Per kernel: engine clock (GRBM_GUI_ACTIVE, summed over the XCDs, per XCD,
+    over the dispatch duration), MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES
+    over SIMDs x engine cycles), and the bf16 rate those two imply."""
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    dur = defaultdict(dict)
+    for kname, cname, val, disp, d in cur.execute(
+            "select kernel_name, counter_name, value, dispatch_id, duration from counters_collection"):
+        k = short(kname)
+        per[k][disp][cname] += float(val)
+        dur[k][disp] = float(d)
+    res = {}
+    out.write(f"{'kernel':<66} {'dispatches':>10} {'avg_us':>9} {'clock_GHz':>9} {'mfma_busy':>9} "
+              f"{'implied_TFLOP/s':>15}\n")
+    for k, disps in sorted(per.items()):
+        rows = [(c, dur[k][d]) for d, c in disps.items()
+                if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c and dur[k][d] > 0]
+        if not rows:
+            continue
+        cyc = [c["GRBM_GUI_ACTIVE"] / XCDS for c, _ in rows]
+        clock = sum(cy / d for cy, (_, d) in zip(cyc, rows)) / len(rows)
+        busy = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cy) for cy, (c, _) in zip(cyc, rows)) / len(rows)
+        avg_us = sum(d for _, d in rows) / len(rows) / 1e3
+        implied = busy * PEAK_TFLOPS * clock / PEAK_GHZ
+        res[k] = {"dispatches": len(rows), "avg_us": avg_us, "clock_ghz": clock, "mfma_busy": busy,
+                  "implied_tflops": implied}
+        out.write(f"{k:<66} {len(rows):>10} {avg_us:>9.1f} {clock:>9.3f} {busy:>9.3f} {implied:>15.1f}\n")
+    return res
+
+
 def traffic(fetch_db: str, write_db: str, copy_kernel: str, copy_bytes: int, out=sys.stdout):
     """HBM bytes per launch, each counter scaled by its reading on the copy."""
     fetch = counter_per_dispatch(fetch_db, "FETCH_SIZE")
@@ -113,6 +152,7 @@ def main():
     ap.add_argument("--by-grid", action="store_true")
     ap.add_argument("--pmc", action="store_true")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--mfma", metavar="MFMA_DB")
     ap.add_argument("--copy-kernel", default="elementwise")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--json", default=None)
@@ -127,6 +167,8 @@ def main():
             res["source_hash"] = a.source_hash
             with open(a.json, "w") as f:
                 json.dump(res, f, indent=1)
+    elif a.mfma:
+        mfma_util(a.mfma)
     elif a.pmc:
         summarize_pmc(a.db)
     else:
