@@ -105,7 +105,9 @@ def mfma_util(db: str, out=sys.stdout):
     for k, disps in sorted(per.items()):
         rows = [(c, dur[k][d]) for d, c in disps.items()
                 if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c and dur[k][d] > 0]
-        if not rows:
+        # kernels without MFMA work (copies, the split-K sum) are short next to
+        # the counters' sampling, so their clock would not mean anything
+        if not rows or not any(c["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 for c, _ in rows):
             continue
         cyc = [c["GRBM_GUI_ACTIVE"] / XCDS for c, _ in rows]
         clock = sum(cy / d for cy, (_, d) in zip(cyc, rows)) / len(rows)
