@@ -98,9 +98,10 @@ def log(msg):
 class Layer:
     """Device buffers of one FC shard and the three calls of a step."""
 
-    def __init__(self, g, X, W, dY, torch, F):
+    def __init__(self, g, X, W, dY, torch, F, xo=0, wo=0):
         self.g, self.F = g, F
-        self.X, self.W, self.dY = X, W, dY
+        self.X, self.W, self.dY = X, W, dY  # X, W stored in orders xo, wo (0 row-, 1 column-major)
+        self.xo, self.wo = xo, wo
         self.Y = torch.empty((g.M, g.N), dtype=torch.bfloat16, device="cuda")
         self.dX = torch.empty((g.M, g.K), dtype=torch.bfloat16, device="cuda")
         self.dW = torch.empty((g.K, g.N), dtype=torch.bfloat16, device="cuda")
@@ -109,18 +110,21 @@ class Layer:
     def calls(self):
         F = self.F
         if self.dW32 is not None:
-            dw = lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW32, out_dtype=F.OUT_F32_ACC)  # noqa: E731
+            dw = lambda: F.fc_bwd_weight(self.X, self.dY, self.xo, out=self.dW32,  # noqa: E731
+                                         out_dtype=F.OUT_F32_ACC)
         else:
-            dw = lambda: F.fc_bwd_weight(self.X, self.dY, out=self.dW)  # noqa: E731
+            dw = lambda: F.fc_bwd_weight(self.X, self.dY, self.xo, out=self.dW)  # noqa: E731
         return [
-            ("fwd", F.OP_FWD, lambda: F.fc_fwd(self.X, self.W, out=self.Y)),
-            ("bwd_data", F.OP_BWD_DATA, lambda: F.fc_bwd_data(self.dY, self.W, out=self.dX)),
+            ("fwd", F.OP_FWD, lambda: F.fc_fwd(self.X, self.W, self.xo, self.wo, out=self.Y)),
+            ("bwd_data", F.OP_BWD_DATA, lambda: F.fc_bwd_data(self.dY, self.W, self.wo, out=self.dX)),
             ("bwd_weight", F.OP_BWD_WEIGHT, dw),
         ]
 
 
-def make_layers(workload, torch, F, I, host_inputs):
+def make_layers(workload, torch, F, I, host_inputs, xo=0, wo=0):
     import numpy as np
+    if host_inputs and (xo or wo):
+        raise ValueError("host inputs are generated row-major only")
     layers = []
     for gi, g in enumerate(I.WORKLOADS[workload], start=1):
         if host_inputs:
@@ -131,7 +135,9 @@ def make_layers(workload, torch, F, I, host_inputs):
         else:
             gen = torch.Generator(device="cuda").manual_seed(1000 * workload + gi)
             rn = lambda r, c, s: (torch.randn((r, c), device="cuda", generator=gen) * s).to(torch.bfloat16)  # noqa
-            layers.append(Layer(g, rn(g.M, g.K, g.sx), rn(g.K, g.N, g.sw), rn(g.M, g.N, g.sdy), torch, F))
+            X = rn(g.M, g.K, g.sx) if xo == 0 else rn(g.K, g.M, g.sx)
+            W = rn(g.K, g.N, g.sw) if wo == 0 else rn(g.N, g.K, g.sw)
+            layers.append(Layer(g, X, W, rn(g.M, g.N, g.sdy), torch, F, xo, wo))
     return layers
 
 
@@ -390,6 +396,23 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         result["large_shard_context"] = extra
+        # the layout sweep: the skinny shard in each storage-order pair
+        sweep = {}
+        for xo, wo in I.ORDER_PAIRS:
+            Ls = make_layers(4, torch, F, I, host_inputs=False, xo=xo, wo=wo)
+            if not args.no_tune:
+                for L in Ls:
+                    F.fc_tune(L.g.M, L.g.K, L.g.N, xo, wo)
+            wms, _, _ = run_timed(Ls, 10, 3, torch)
+            wf = step_flops(Ls)
+            key = f"X {'row' if xo == 0 else 'col'}, W {'row' if wo == 0 else 'col'}"
+            sweep[key] = {"tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
+                          "plans": [F.fc_plan_describe(op, L.g.M, L.g.K, L.g.N, xo, wo)["kernel"]
+                                    for L in Ls for op in (F.OP_FWD, F.OP_BWD_DATA, F.OP_BWD_WEIGHT)]}
+            log(f"workload 4 {key}: {sweep[key]['tflops']} TFLOP/s")
+            del Ls
+            torch.cuda.empty_cache()
+        result["layout_sweep_context"] = {"workload": WORKLOAD_NAMES[4], "gemms_per_step": 3, "by_orders": sweep}
         # the same step with every dW added into an fp32 gradient buffer
         # (accumulation over micro-batches), for context
         Ls = make_layers(args.workload, torch, F, I, host_inputs=False)
