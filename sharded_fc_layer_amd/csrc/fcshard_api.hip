@@ -622,14 +622,17 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         // candidate plans
         std::vector<int> cand;
         int64_t need = 0;
-        for (int id = 0; id < kNumPlans; ++id) {
-            const Plan pl = decode_plan(id);
-            if (!plan_applies(p, pl)) continue;
-            if (!exhaustive && pl.split > 1 && pl.copy != 0) continue;
-            // the simple kernels only win on unaligned shapes
-            if (!exhaustive && pl.family == 1 && problem_aligned(p)) continue;
-            cand.push_back(id);
-            need = std::max(need, ws_layout(p, pl).total);
+        for (int pass = 0; pass < 2 && cand.empty(); ++pass) {
+            for (int id = 0; id < kNumPlans; ++id) {
+                const Plan pl = decode_plan(id);
+                if (!plan_applies(p, pl)) continue;
+                if (!exhaustive && pl.split > 1 && pl.copy != 0) continue;
+                // the simple kernels only win on unaligned shapes, or where no
+                // other family applies (an operand of 2 GiB or more): second pass
+                if (!exhaustive && pass == 0 && pl.family == 1 && problem_aligned(p)) continue;
+                cand.push_back(id);
+                need = std::max(need, ws_layout(p, pl).total);
+            }
         }
         {
             std::lock_guard<std::mutex> lk(g_mu);

@@ -36,6 +36,10 @@ Readings where the pages are silent:
 * Time per batch = compute + communication (no overlap), as the pages' model
   sums collective times; max(compute, communication) is reported beside it as
   the bound that perfect overlap would reach.
+* Memory: a grid fits if its FC parameters per GPU (all FC weights over
+  Gx Gy Gz; data parallelism replicates) times 16 bytes (bf16 weight and
+  gradient, fp32 master weight, two fp32 Adam moments) fit in the GPU's HBM.
+  Activations are not counted. Grids that do not fit rank after those that do.
 
 Usage (the plan file is written on a GPU; ranking needs only the CPU):
   python -m sharded_fc_layer_amd.perf_model measure --out plans.txt [model] [--gpus G]
@@ -113,6 +117,8 @@ class Machine:
     gpus_per_node: int = 8
     link_gbs: float = 153.0  # one xGMI link, one direction, GB/s
     inter_gbs: float = 50.0  # per GPU between nodes, GB/s (one 400 Gb/s NIC per GPU)
+    hbm_gb: float = 288.0
+    bytes_per_param: int = 16  # bf16 weight + bf16 gradient + fp32 master + two fp32 Adam moments
 
 
 def _coords(grid: Grid, rank: int) -> Dict[str, int]:
@@ -248,8 +254,11 @@ def predict(model: Model, grid: Grid, m: Machine, times: GemmTimes) -> Optional[
             t = s.count * collective_ms(c, grid, m)
             comm += t
             parts[c.name] = parts.get(c.name, 0.0) + t
+    params = sum(s.count * s.K * s.N for s in sh)  # this GPU's weight shards (before the Z split)
+    state_gb = params / grid.z * m.bytes_per_param / 1e9
     return {"grid": str(grid), "compute_ms": compute, "comm_ms": comm, "total_ms": compute + comm,
-            "overlap_bound_ms": max(compute, comm), "comm_parts_ms": parts}
+            "overlap_bound_ms": max(compute, comm), "comm_parts_ms": parts,
+            "weight_state_gb": state_gb, "fits": state_gb <= m.hbm_gb}
 
 
 def rank(model: Model, gpus: int, m: Machine, times: GemmTimes) -> Tuple[List[dict], List[Tuple[str, tuple]]]:
@@ -263,7 +272,7 @@ def rank(model: Model, gpus: int, m: Machine, times: GemmTimes) -> Tuple[List[di
             continue
         if r is not None:
             done.append(r)
-    done.sort(key=lambda r: (r["total_ms"], r["grid"]))
+    done.sort(key=lambda r: (not r["fits"], r["total_ms"], r["grid"]))
     return done, missing
 
 
@@ -398,10 +407,11 @@ def main(argv: Optional[Iterable[str]] = None) -> int:
         return 0
     print(f"{model.name}: hidden {model.hidden}, ffn {model.ffn}, {model.layers} layers, vocab {model.vocab}, "
           f"{model.tokens} tokens per batch, {a.gpus} GPUs")
-    print(f"{'rank':>4} {'grid d x y z':>13} {'compute ms':>11} {'comm ms':>9} {'total ms':>9} {'overlap ms':>10}")
+    print(f"{'rank':>4} {'grid d x y z':>13} {'compute ms':>11} {'comm ms':>9} {'total ms':>9} {'overlap ms':>10} "
+          f"{'state GB':>9}")
     for i, r in enumerate(done, 1):
         print(f"{i:4d} {r['grid']:>13} {r['compute_ms']:11.3f} {r['comm_ms']:9.3f} {r['total_ms']:9.3f} "
-              f"{r['overlap_bound_ms']:10.3f}")
+              f"{r['overlap_bound_ms']:10.3f} {r['weight_state_gb']:9.1f}{'' if r['fits'] else '  does not fit'}")
     for g, k in missing:
         print(f"     {g:>13} no measured time for {k}")
     return 0

@@ -268,18 +268,24 @@ def test_operands_of_2_gib_and_more():
          "dY": I.integer_bf16_chunked([31, 3], (M, N))}
     c = Case(d, ROW, ROW)
     rng = np.random.default_rng(31)
-    for op in OPS:
-        desc = F.fc_plan_describe(op_code(op), M, K, N)
-        what = f"max-size {op} {desc['kernel']}"
-        log(what)
-        if op != "bwd_data":
-            assert desc["kernel"].startswith("gemm_bf16_kernel"), what
-        Gt = c.gpu(op, F.OUT_BF16)
-        rows, cols = _sample(Gt.shape[0], 24, rng), _sample(Gt.shape[1], 96, rng)
-        O, _ = c.oracle(op, rows, cols)
-        G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
-        assert_exact(G, O, F.OUT_BF16, what)
-        del Gt
+    for plans in ("default", "tuned"):
+        if plans == "tuned":
+            # the quick search still has candidates where only the simple kernel applies
+            F.fc_tune(M, K, N)
+        for op in OPS:
+            desc = F.fc_plan_describe(op_code(op), M, K, N)
+            what = f"max-size {plans} {op} {desc['kernel']} split={desc['split']}"
+            log(what)
+            if op != "bwd_data":
+                assert desc["kernel"].startswith("gemm_bf16_kernel"), what
+            if plans == "tuned":
+                assert desc.get("tuned_ms", 0) > 0, what
+            Gt = c.gpu(op, F.OUT_BF16)
+            rows, cols = _sample(Gt.shape[0], 24, rng), _sample(Gt.shape[1], 96, rng)
+            O, _ = c.oracle(op, rows, cols)
+            G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+            assert_exact(G, O, F.OUT_BF16, what)
+            del Gt
     del c
     torch.cuda.empty_cache()
 

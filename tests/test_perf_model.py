@@ -188,3 +188,18 @@ def test_times_from_plan_file():
         open(p, "w").write("\n".join(lines) + "\n")
         t = PM.times_from_plan_file(p)
     assert t == {("fwd", 512, 64, 192): 0.0125, ("bwd_weight", 512, 64, 192): 0.02}
+
+
+def test_weight_state_memory():
+    # 405B-like FC weights: 126 layers x (3h^2 + h^2 + 2 h f) + vocabulary h V
+    h, f, V, Lr = 16384, 53248, 128256, 126
+    model = PM.Model("405b-like", h, f, Lr, V, 16384)
+    t = _times(model, 16, lambda op, M, K, N: 1e-9 * M * K * N)
+    full = Lr * (3 * h * h + h * h + 2 * h * f) + h * V
+    for g in (PM.Grid(16, 1, 1, 1), PM.Grid(1, 2, 4, 2), PM.Grid(2, 2, 2, 2)):
+        r = PM.predict(model, g, PM.Machine(), t)
+        assert r["weight_state_gb"] == pytest.approx(full / (g.x * g.y * g.z) * 16 / 1e9, rel=1e-12)
+    done, _ = PM.rank(model, 16, PM.Machine(), t)
+    fits = [r["fits"] for r in done]
+    assert fits == sorted(fits, reverse=True)  # grids that fit come first
+    assert not PM.predict(model, PM.Grid(16, 1, 1, 1), PM.Machine(), t)["fits"]
