@@ -1,0 +1,88 @@
+"""The profiling harness's arithmetic on small synthetic rocprofv3 databases
+(CPU): kernel-trace averages, HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by
+a copy of known size, and the engine clock and MFMA busy fraction."""
+from __future__ import annotations
+
+import io
+import os
+import sqlite3
+import tempfile
+
+import pytest
+
+from sharded_fc_layer_amd import rocprof_summary as R
+
+GEMM = "void fcs::(anonymous namespace)::gemm_w4k64_kernel<false, true, false>(fcs::GemmArgs)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16_copy_kernel_cuda>(int)"
+
+
+def _counter_db(path, rows):
+    """rows: (kernel_name, counter_name, value, dispatch_id, duration_ns)"""
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real, "
+                "dispatch_id integer, duration integer)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_kernel_trace_averages():
+    with tempfile.TemporaryDirectory() as d:
+        db = os.path.join(d, "t.db")
+        con = sqlite3.connect(db)
+        con.execute("create table kernels (id integer, name text, duration integer, grid_x integer, grid_y integer, "
+                    "grid_z integer, start integer)")
+        con.executemany("insert into kernels values (?, ?, ?, ?, ?, ?, ?)",
+                        [(1, GEMM, 100_000, 65536, 1, 1, 0), (2, GEMM, 300_000, 65536, 1, 1, 1),
+                         (3, COPY, 50_000, 1024, 1, 1, 2)])
+        con.commit()
+        con.close()
+        out = io.StringIO()
+        R.summarize(db, False, out)
+    line = next(l for l in out.getvalue().splitlines() if l.startswith("gemm_w4k64_kernel"))
+    f = line.split()
+    # calls 2, avg 200 us, min 100, max 300, total 0.4 ms, 400 of 450 us = 88.89 %
+    assert f[-6:] == ["2", "200.00", "100.00", "300.00", "0.400", "88.89"]
+
+
+def test_traffic_scales_each_counter_by_the_copy():
+    gib = 1 << 30
+    # the copy reads and writes 1 GiB; FETCH_SIZE reads half of it (KiB), WRITE_SIZE all of it
+    rows_f = [(COPY, "FETCH_SIZE", gib / 2 / 1024, 1, 1), (GEMM, "FETCH_SIZE", 100_000.0, 2, 1),
+              (GEMM, "FETCH_SIZE", 300_000.0, 3, 1)]
+    rows_w = [(COPY, "WRITE_SIZE", gib / 1024, 1, 1), (GEMM, "WRITE_SIZE", 50_000.0, 2, 1),
+              (GEMM, "WRITE_SIZE", 50_000.0, 3, 1)]
+    with tempfile.TemporaryDirectory() as d:
+        f, w = os.path.join(d, "f.db"), os.path.join(d, "w.db")
+        _counter_db(f, rows_f)
+        _counter_db(w, rows_w)
+        res = R.traffic(f, w, "elementwise", gib, io.StringIO())
+    assert res["fetch_scale"] == pytest.approx(2.0) and res["write_scale"] == pytest.approx(1.0)
+    k = res["kernels"]["gemm_w4k64_kernel<false, true, false>"]
+    assert k["launches"] == 2
+    assert k["fetch_bytes_per_launch"] == pytest.approx(200_000 * 1024 * 2.0)
+    assert k["write_bytes_per_launch"] == pytest.approx(50_000 * 1024 * 1.0)
+    assert k["hbm_bytes_per_launch"] == pytest.approx(k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"])
+
+
+def test_mfma_busy_and_clock():
+    dur = 100_000  # ns
+    clock = 2.0  # GHz -> 200 000 engine cycles
+    cycles = dur * clock
+    busy = 0.75
+    rows = []
+    for disp in (1, 2):
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs; the MFMA counter over 1024 SIMDs
+        rows.append((GEMM, "GRBM_GUI_ACTIVE", cycles * R.XCDS, disp, dur))
+        rows.append((GEMM, "SQ_VALU_MFMA_BUSY_CYCLES", busy * R.SIMDS * cycles, disp, dur))
+    rows.append((COPY, "GRBM_GUI_ACTIVE", 8 * 1000.0, 3, 500))
+    rows.append((COPY, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0, 3, 500))
+    with tempfile.TemporaryDirectory() as d:
+        db = os.path.join(d, "m.db")
+        _counter_db(db, rows)
+        res = R.mfma_util(db, io.StringIO())
+    assert set(res) == {"gemm_w4k64_kernel<false, true, false>"}  # the copy has no MFMA work
+    r = res["gemm_w4k64_kernel<false, true, false>"]
+    assert r["dispatches"] == 2 and r["avg_us"] == pytest.approx(100.0)
+    assert r["clock_ghz"] == pytest.approx(clock) and r["mfma_busy"] == pytest.approx(busy)
+    assert r["implied_tflops"] == pytest.approx(busy * 2500.0 * clock / 2.4)
