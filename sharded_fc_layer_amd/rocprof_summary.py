@@ -7,7 +7,9 @@ per-dispatch averages of each counter. With --traffic it combines a
 FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per launch of each kernel,
 scaled by what the same counters read for a plain copy of known size. With
 --mfma it turns a run with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE into
-each kernel's engine clock and MFMA busy fraction.
+each kernel's engine clock and MFMA busy fraction, and, with
+SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA operations / 512), the flops the
+hardware executed per launch.
 Usage:
 
   python -m sharded_fc_layer_amd.rocprof_summary RESULTS.db [--by-grid] [--pmc]
@@ -101,7 +103,7 @@ def mfma_util(db: str, out=sys.stdout):
         dur[k][disp] = float(d)
     res = {}
     out.write(f"{'kernel':<66} {'dispatches':>10} {'avg_us':>9} {'clock_GHz':>9} {'mfma_busy':>9} "
-              f"{'implied_TFLOP/s':>15}\n")
+              f"{'implied_TFLOP/s':>15} {'hw_GFLOP/launch':>15}\n")
     for k, disps in sorted(per.items()):
         rows = [(c, dur[k][d]) for d, c in disps.items()
                 if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c and dur[k][d] > 0]
@@ -114,9 +116,12 @@ def mfma_util(db: str, out=sys.stdout):
         busy = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cy) for cy, (c, _) in zip(cyc, rows)) / len(rows)
         avg_us = sum(d for _, d in rows) / len(rows) / 1e3
         implied = busy * PEAK_TFLOPS * clock / PEAK_GHZ
+        mops = [c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") for c, _ in rows]
+        hw = sum(mops) * 512 / len(mops) if all(m is not None for m in mops) else None
         res[k] = {"dispatches": len(rows), "avg_us": avg_us, "clock_ghz": clock, "mfma_busy": busy,
-                  "implied_tflops": implied}
-        out.write(f"{k:<66} {len(rows):>10} {avg_us:>9.1f} {clock:>9.3f} {busy:>9.3f} {implied:>15.1f}\n")
+                  "implied_tflops": implied, "hw_flops_per_launch": hw}
+        hw_s = f"{hw / 1e9:>15.3f}" if hw is not None else f"{'-':>15}"
+        out.write(f"{k:<66} {len(rows):>10} {avg_us:>9.1f} {clock:>9.3f} {busy:>9.3f} {implied:>15.1f} {hw_s}\n")
     return res
 
 

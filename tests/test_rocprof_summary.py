@@ -75,6 +75,7 @@ def test_mfma_busy_and_clock():
         # GRBM_GUI_ACTIVE comes summed over the 8 XCDs; the MFMA counter over 1024 SIMDs
         rows.append((GEMM, "GRBM_GUI_ACTIVE", cycles * R.XCDS, disp, dur))
         rows.append((GEMM, "SQ_VALU_MFMA_BUSY_CYCLES", busy * R.SIMDS * cycles, disp, dur))
+        rows.append((GEMM, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2 * 8192 * 2048 * 2048 / 512, disp, dur))
     rows.append((COPY, "GRBM_GUI_ACTIVE", 8 * 1000.0, 3, 500))
     rows.append((COPY, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0, 3, 500))
     with tempfile.TemporaryDirectory() as d:
@@ -86,3 +87,4 @@ def test_mfma_busy_and_clock():
     assert r["dispatches"] == 2 and r["avg_us"] == pytest.approx(100.0)
     assert r["clock_ghz"] == pytest.approx(clock) and r["mfma_busy"] == pytest.approx(busy)
     assert r["implied_tflops"] == pytest.approx(busy * 2500.0 * clock / 2.4)
+    assert r["hw_flops_per_launch"] == pytest.approx(2 * 8192 * 2048 * 2048)
