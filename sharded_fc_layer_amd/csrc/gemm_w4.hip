@@ -176,29 +176,19 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, smem + wave * (128 * 256));
 }
 
-// Placement of a 64-MFMA step's 16 fragment reads and NL loads: the index of
-// the read (0..15) or load (0..NL-1) issued right after MFMA u, or -1.
-// 0: reads after MFMAs 0..15, then the loads evenly over the rest;
-// 1: the loads first, after every second MFMA, then the reads;
-// 2: one load after every fourth MFMA, reads after the two that follow;
-// 3: as 2 with a load after every third MFMA and one read after the next;
-// 4: as 2, and a step without loads spreads its reads over every second MFMA.
-__device__ constexpr int w64_read_after(int sched, int nl, int u) {
-    if (nl == 0) return sched == 4 ? ((u % 2 == 0 && u / 2 < 16) ? u / 2 : -1) : (u < 16 ? u : -1);
-    if (sched == 0) return u < 16 ? u : -1;
-    if (sched == 1) return (u >= 2 * nl && u < 2 * nl + 16) ? u - 2 * nl : -1;
-    if (sched == 3) return (u % 3 == 1 && u / 3 < 16) ? u / 3 : -1;
+// Placement of a 64-MFMA step's 16 fragment reads and NL loads (NL <= 16):
+// the index of the read (0..15) or load (0..NL-1) issued right after MFMA u,
+// or -1. With loads, one load after every fourth MFMA and the reads after the
+// two MFMAs that follow it; without loads, the reads after MFMAs 0..15.
+// (Measured and slower or equal: the reads first and the loads spread over
+// the rest; the loads first, one after every second MFMA; a load after every
+// third MFMA; a loadless step's reads after every second MFMA.)
+__device__ constexpr int w64_read_after(int nl, int u) {
+    if (nl == 0) return u < 16 ? u : -1;
     return (u % 4 != 0 && u % 4 != 3 && u / 4 < 8) ? 2 * (u / 4) + (u % 4) - 1 : -1;
 }
-__device__ constexpr int w64_load_after(int sched, int nl, int u) {
-    if (nl == 0) return -1;
-    if (sched == 0) {
-        const int gap = 48 / nl;
-        return (u >= 16 && (u - 16) % gap == 0 && (u - 16) / gap < nl) ? (u - 16) / gap : -1;
-    }
-    if (sched == 1) return (u % 2 == 0 && u / 2 < nl) ? u / 2 : -1;
-    if (sched == 3) return (u % 3 == 0 && u / 3 < nl) ? u / 3 : -1;
-    return (u % 4 == 0 && u / 4 < nl) ? u / 4 : -1;
+__device__ constexpr int w64_load_after(int nl, int u) {
+    return (nl > 0 && u % 4 == 0 && u / 4 < nl) ? u / 4 : -1;
 }
 
 // Orders every compiler write of the accumulators (their zero
@@ -244,8 +234,6 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     constexpr int kABytes = 256 * BKP * 2;                                       // 32 KB per operand
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;                                // 8
     constexpr int kLoads = kLA + DmaPP<B_OC, BKP>::kInstr;                       // per wave per stage
-    constexpr int kSched = 2;  // placement of reads and loads in a step (w64_read_after)
-    constexpr bool kSplitLoads = false;  // a stage's loads over two steps (slower: too little time to land)
     // one array per slot and operand: the compiler tracks each array's
     // direct-to-LDS writes separately, so an LDS read waits only for the
     // loads into the array it reads
@@ -291,13 +279,13 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         constexpr int nl_ = la_ + (((LOADS) & 2) ? kLoads - kLA : 0);                                  \
         _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
             mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
-            const int r_ = w64_read_after(kSched, nl_, u);                                              \
+            const int r_ = w64_read_after(nl_, u);                                              \
             if (r_ >= 0 && r_ < 8) {                                                                   \
                 fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
             } else if (r_ >= 8) {                                                                      \
                 fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
             }                                                                                          \
-            const int l_ = w64_load_after(kSched, nl_, u);                                             \
+            const int l_ = w64_load_after(nl_, u);                                             \
             if (l_ >= 0 && l_ < la_)                                                                   \
                 da.issue_one(w.ra, LA, sa_, wave, l_);                                                 \
             else if (l_ >= la_)                                                                        \
@@ -306,27 +294,21 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     }
     // stage T in slot (XA, XB), stage T + 1 in slot (YA, YB). Step 1 opens with
     // the barrier that certifies stage T + 1 and frees slot X (its last reads,
-    // of step 1, were issued during step 0). kSplitLoads: the A half of stage
-    // T + 2 is loaded during step 1 and its B half during step 0 of stage
-    // T + 1 (slot Y's B tile is free since the barrier of stage T - 1), which
-    // halves the address unit's load rate; otherwise both halves in step 1.
+    // of step 1, were issued during step 0), then loads stage T + 2 into slot X.
+    // (Splitting a stage's loads over both steps halved the time they had to
+    // land and was slower.)
 #define FCW64_STAGE(T, XA, XB, YA, YB)                                                    \
     {                                                                                     \
-        FCW64_STEP(0, 1, XA, XB, 1, kSplitLoads ? 2 : 0, YA, YB, (T) + 1)                 \
+        FCW64_STEP(0, 1, XA, XB, 1, 0, YA, YB, (T) + 1)                                   \
         waitcnt<0, 0>();                                                                  \
         __builtin_amdgcn_s_barrier();                                                     \
-        FCW64_STEP(1, 0, YA, YB, 0, kSplitLoads ? 1 : 3, XA, XB, (T) + 2)                 \
+        FCW64_STEP(1, 0, YA, YB, 0, 3, XA, XB, (T) + 2)                                   \
     }
 
     if (nkt > 0) {
         FCW64_ISSUE(a0, b0, 0)
-        if constexpr (kSplitLoads) {
-            FCW64_STEPS(1)
-            da.issue_full(w.ra, a1, sa_, wave);
-        } else {
-            FCW64_ISSUE(a1, b1, 1)
-        }
-        waitcnt<kSplitLoads ? kLA : kLoads, 0>();
+        FCW64_ISSUE(a1, b1, 1)
+        waitcnt<kLoads, 0>();
         __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(a0, wm0 + i * MF, 0, lane);
@@ -372,7 +354,6 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     constexpr int kT = 256 * BKP * 2;  // 32 KB per operand tile
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
     constexpr int kLB = DmaPP<B_OC, BKP>::kInstr;
-    constexpr int kSched = 2;
     __shared__ __attribute__((aligned(1024))) char ta0[kT];
     __shared__ __attribute__((aligned(1024))) char ta1[kT];
     __shared__ __attribute__((aligned(1024))) char ta2[kT];
@@ -410,13 +391,13 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         constexpr int nl_ = (LOADS) ? kLA + kLB : 0;                                                   \
         _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
             mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
-            const int r_ = w64_read_after(kSched, nl_, u);                                             \
+            const int r_ = w64_read_after(nl_, u);                                             \
             if (r_ >= 0 && r_ < 8) {                                                                   \
                 fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
             } else if (r_ >= 8) {                                                                      \
                 fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
             }                                                                                          \
-            const int l_ = w64_load_after(kSched, nl_, u);                                             \
+            const int l_ = w64_load_after(nl_, u);                                             \
             if (l_ >= 0 && l_ < kLB)                                                                   \
                 db.issue_one(rb_, LB, sb_, wave, l_);                                                  \
             else if (l_ >= kLB)                                                                        \
