@@ -397,7 +397,7 @@ fc_status grow_workspace(int dev, int64_t bytes) {
     return FC_OK;
 }
 
-std::string describe(const Problem& p, int id, int64_t ws_have) {
+std::string describe(const Problem& p, int id) {
     const Plan pl = decode_plan(id);
     Problem q = p;
     if ((pl.copy & 1) && q.a_oc) q.a_oc = false, q.A = nullptr;
@@ -418,7 +418,6 @@ std::string describe(const Problem& p, int id, int64_t ws_have) {
     std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname,
                   kTiles[aligned ? pl.tile : kUnalignedTile].name, slices, pl.copy,
                   (long long)ws_layout(p, pl).total);
-    (void)ws_have;
     return buf;
 }
 
@@ -555,7 +554,7 @@ fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x
     if (it != g_plans.end()) id = it->second.id, ms = it->second.ms;
     if (id >= 0 && ws_layout(p, decode_plan(id)).total > g_dev[dev].ws_bytes) id = -1, ms = -1.0f;
     if (id < 0) id = default_plan(p);
-    std::string s = describe(p, id, g_dev[dev].ws_bytes);
+    std::string s = describe(p, id);
     if (ms >= 0.0f) {
         char t[48];
         std::snprintf(t, sizeof t, " tuned_ms=%.6f", ms);
@@ -671,8 +670,8 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         if (log_enabled()) {
             for (auto& t : times)
                 std::fprintf(stderr, "[fcshard] tune op=%d M=%lld K=%lld N=%lld %s: %.4f ms\n", op, (long long)M,
-                             (long long)K, (long long)N, describe(p, t.first, 0).c_str(), t.second);
-            std::fprintf(stderr, "[fcshard] tune op=%d pick %s\n", op, pick >= 0 ? describe(p, pick, 0).c_str() : "none");
+                             (long long)K, (long long)N, describe(p, t.first).c_str(), t.second);
+            std::fprintf(stderr, "[fcshard] tune op=%d pick %s\n", op, pick >= 0 ? describe(p, pick).c_str() : "none");
         }
         if (pick >= 0) {
             float pick_ms = -1.0f;
