@@ -40,7 +40,9 @@ constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
 // 6-8: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
 // 32-value stages (6), 64-value stages in two LDS slots (7) or in a ring of
-// three A and two B tiles (8)
+// three A and two B tiles (8). Families 7 and 8 also run 256 x 192 block
+// tiles (tile 2; 128 x 96 per wave): where 256 x 256 tiles leave CUs idle
+// (192 tiles on 256 CUs), 256 x 192 ones may fill them (256 tiles).
 constexpr int kNumFamilies = 9;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
@@ -66,6 +68,9 @@ Plan decode_plan(int id) {
 int encode_plan(int tile, int split_idx, int copy, int family) {
     return tile + kNumTiles * (split_idx + kNumSplits * (copy + kNumCopy * family));
 }
+
+// block-tile width (output columns) of a one-wave-per-SIMD plan
+int w4_bn(const Plan& pl) { return pl.family > kFamilyW4 && pl.tile == 2 ? 192 : 256; }
 
 // One GEMM in kernel terms, resolved from an ABI call.
 struct Problem {
@@ -131,7 +136,7 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 1) || (uintptr_t)p.A % 16 == 0) &&
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
-    if (pl.family >= 2 && pl.tile != 0) return false;
+    if (pl.family >= 2 && pl.tile != 0 && !(pl.family > kFamilyW4 && pl.tile == 2)) return false;
     if (pl.family >= kFamilyW4) {  // whole stages (pairs of 32- or 64-value stages for 6 and 7)
         const int64_t q = pl.family == kFamilyW4 ? 64 : pl.family == kFamilyW4 + 1 ? 128 : 64;
         int64_t ks;
@@ -279,7 +284,7 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
         g.C = part;
         g.c_split_stride = p.M * p.N;
         e = pl.family == 0            ? launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, true, g, s)
-            : pl.family >= kFamilyW4  ? launch_gemm_w4(pl.family - kFamilyW4, p.a_oc, p.b_oc, true, g, s)
+            : pl.family >= kFamilyW4  ? launch_gemm_w4(pl.family - kFamilyW4, w4_bn(pl), p.a_oc, p.b_oc, true, g, s)
             : pl.family >= 2          ? launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, true, g, s)
                              : launch_gemm(pl.tile, p.a_oc, p.b_oc, true, aligned, g, s);
         if (e != hipSuccess) return e;
@@ -289,7 +294,7 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
     g.c_split_stride = 0;
     g.accumulate = p.accumulate ? 1 : 0;
     if (pl.family == 0) return launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, p.out_f32, g, s);
-    if (pl.family >= kFamilyW4) return launch_gemm_w4(pl.family - kFamilyW4, p.a_oc, p.b_oc, p.out_f32, g, s);
+    if (pl.family >= kFamilyW4) return launch_gemm_w4(pl.family - kFamilyW4, w4_bn(pl), p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= 2) return launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, p.out_f32, g, s);
     return launch_gemm(pl.tile, p.a_oc, p.b_oc, p.out_f32, aligned, g, s);
 }
@@ -410,13 +415,14 @@ std::string describe(const Problem& p, int id) {
                          (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
     const bool f32 = slices > 1 ? true : p.out_f32;
     const char* kname = pl.family == 0            ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
-                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, q.a_oc, q.b_oc, f32)
+                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, w4_bn(pl), q.a_oc, q.b_oc, f32)
                         : pl.family >= 2          ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
                                          : gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc, f32,
                                                             aligned);
     char buf[512];
-    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname,
-                  kTiles[aligned ? pl.tile : kUnalignedTile].name, slices, pl.copy,
+    const char* tname = w4_bn(pl) == 192 ? "256x192" : kTiles[aligned ? pl.tile : kUnalignedTile].name;
+    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname, tname, slices,
+                  pl.copy,
                   (long long)ws_layout(p, pl).total);
     return buf;
 }

@@ -58,16 +58,16 @@ hipError_t launch_gemm_pingpong(int variant, bool a_oc, bool b_oc, bool out_f32,
                                 hipStream_t stream);
 const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
 
-// Enqueue the 4-wave (one wave per SIMD) GEMM, 256 x 256 tile, 128 x 128
-// per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
+// Enqueue the 4-wave (one wave per SIMD) GEMM, 256 x bn block tile, 128 x
+// bn / 2 per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
 // launch_gemm_pipe, and K a multiple of 64, of 128 for variant 1).
 // variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
 // 2 slots (whole-cache-line rows for reduction-contiguous operands); 2: the
 // same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about
-// two stages to land.
-hipError_t launch_gemm_w4(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+// two stages to land. bn is 256, or 192 for variants 1 and 2.
+hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream);
-const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32);
+const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32);
 
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

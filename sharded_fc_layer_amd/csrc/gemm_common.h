@@ -49,9 +49,21 @@ __device__ __forceinline__ uint32_t rc_slot_k(int i, int c) {
 // (conflict-free; with (k & 3) << 2 alone, rows k and k + 8 shared banks).
 // The 32x32x16 operand reads 4 rows x 64 B per half-wave, conflict-free either way.
 __device__ __forceinline__ int oc_swizzle(int k) { return ((k & 3) << 2) | ((k & 8) >> 2); }
+// Rows of 192 values (384 B, 24 chunks): row k starts on 32-byte bank group
+// 4 (k & 1) (mod 8), and the XOR may only permute chunks within groups of 8.
+// XOR-ing the chunk with 2 t, t = bit 1 of k | (bit 3 of k) << 1, gives the
+// even rows of a half-wave read (k0, k0+2, k0+8, k0+10) four different t, and
+// the odd rows likewise: again 8 different bank groups.
+template <int R>
+__device__ __forceinline__ int oc_swizzle_r(int k) {
+    if constexpr (R == 192)
+        return (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1;
+    else
+        return oc_swizzle(k);
+}
 template <int R>
 __device__ __forceinline__ uint32_t oc_slot(int k, int c) {
-    return k * (R * 2) + ((c ^ oc_swizzle(k)) << 4);
+    return k * (R * 2) + ((c ^ oc_swizzle_r<R>(k)) << 4);
 }
 
 // s_waitcnt with vmcnt = vm, lgkmcnt = lgkm (expcnt not waited)
@@ -122,11 +134,11 @@ __device__ __forceinline__ bf16x8 fragment(const char* region, int r0, int ks, i
     }
 }
 
-// loads of one operand tile (256 rows x BKP reduction values) shared by 4 waves
-template <bool OC, int BKP>
+// loads of one operand tile (R rows x BKP reduction values) shared by 4 waves
+template <bool OC, int BKP, int R = 256>
 struct DmaPP {
     static_assert(BKP == 32 || BKP == 64, "32- or 64-value stages");
-    static constexpr int R = 256;
+    static_assert(R == 256 || (BKP == 64 && R == 192), "tile rows");
     static constexpr int kInstr = R * BKP * 2 / 1024 / 4;  // per wave
     uint32_t base[kInstr];
     int kk[kInstr];
@@ -144,7 +156,7 @@ struct DmaPP {
             } else {
                 constexpr int CPR = R / 8;
                 const int k = p / CPR;
-                const int c = (p % CPR) ^ oc_swizzle(k);
+                const int c = (p % CPR) ^ oc_swizzle_r<R>(k);
                 kk[j] = k;
                 base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
             }
@@ -223,7 +235,7 @@ __device__ __forceinline__ typename AccT<MF>::type mfma_bf16(bf16x8 a, bf16x8 b,
 // 16 x 16 x 32: lane l holds block row l % 16 and reduction values
 // 32 ks + 8 (l / 16) .. +7; for output-contiguous tiles the 16-lane group g
 // reads rows 32 ks + 8 g (+4) with two ds_read_b64_tr_b16.
-template <bool OC, int BKP, int MF>
+template <bool OC, int BKP, int MF, int R = 256>
 __device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks, int lane) {
     if constexpr (MF == 32) {
         return fragment_pp<OC, BKP>(region, r0, ks, lane);
@@ -237,9 +249,9 @@ __device__ __forceinline__ bf16x8 fragment_mf(const char* region, int r0, int ks
         const int k = ks * 32 + 8 * g + (j >> 2);
         const int c = col >> 3, half = (col & 7) << 1;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<256>(k, c) + half));
+            (lds_i16x4_t*)(region + oc_slot<R>(k, c) + half));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(region + oc_slot<256>(k + 4, c) + half));
+            (lds_i16x4_t*)(region + oc_slot<R>(k + 4, c) + half));
         const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8, v);
     }
@@ -278,9 +290,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t
     }
 }
 
-// bf16 epilogue of a 128 x 128 wave tile of 16 x 16 blocks (acc[i][j]: lane
+// bf16 epilogue of a 128 x 16 TN wave tile of 16 x 16 blocks (acc[i][j]: lane
 // holds row 16 i + lane % 16, columns 16 j + 4 (lane / 16) .. +3), staged
-// through `stage`, 32 KB of LDS that this wave alone uses. Written straight
+// through `stage`, 32 KB of LDS that this wave alone uses (rows of 256 B
+// whatever TN; chunks past the tile's columns stay unused). Written straight
 // from the registers, each store instruction would cover 16 rows x 32 B
 // (quarter cache lines); staged, the wave writes its 8-byte pieces into LDS
 // rows of 256 B and reads back 16-byte chunks, so each store writes 4 rows x
@@ -288,14 +301,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t
 // 16-byte chunk index in an LDS row is XOR-swizzled by the row (mod 16):
 // a half-wave's writes (16 rows x 16 B) and a row's reads (16 chunks) then
 // fall on distinct banks. Needs N % 8 == 0 and a 16-byte-aligned C.
+template <int TN>
 __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_t m0, int64_t n0, int wm0, int wn0,
-                                                       int lane, const f32x4 (&acc)[8][8], char* stage) {
+                                                       int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = i * 16 + lr;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < TN; ++j) {
             const int col = j * 16 + lk * 4;
             const uint32_t off = row * 256 + (((col >> 3) ^ (row & 15)) << 4) + ((col & 7) << 1);
             const f32x4 v = acc[i][j];
@@ -308,7 +322,8 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
         const int row = q * 4 + rq;
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
         const int64_t m = m0 + wm0 + row, n = n0 + wn0 + ch * 8;
-        if (m < g.M && n < g.N) *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.N + n) = v;
+        if (m < g.M && n < g.N && (TN == 8 || ch < 2 * TN))
+            *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.N + n) = v;
     }
 }
 
@@ -319,8 +334,9 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
 // banks. Each store writes 2 rows x 512 B of whole lines; an accumulating
 // output is read back the same way and added. Within one wave, LDS accesses
 // complete in order, so the second pass may overwrite what the first read.
+template <int TN>
 __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int slice, int64_t m0, int64_t n0, int wm0,
-                                                      int wn0, int lane, const f32x4 (&acc)[8][8], char* stage) {
+                                                      int wn0, int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
     float* C = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride;
 #pragma unroll
@@ -329,7 +345,7 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
         for (int i = 0; i < 4; ++i) {
             const int row = i * 16 + lr;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < TN; ++j) {
                 const int ch = 4 * j + lk;
                 *reinterpret_cast<f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
             }
@@ -340,7 +356,7 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
             const int row = 2 * q + rq;
             f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
             const int64_t m = m0 + wm0 + 64 * h + row, n = n0 + wn0 + 4 * ch;
-            if (m < g.M && n < g.N) {
+            if (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN)) {
                 float* c = C + m * g.N + n;
                 if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
                 *reinterpret_cast<f32x4*>(c) = v;

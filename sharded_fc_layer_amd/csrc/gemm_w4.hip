@@ -55,15 +55,15 @@ struct W4Setup {
     __amdgpu_buffer_rsrc_t ra, rb;
 };
 
-template <bool A_OC, bool B_OC, int BKP>
+template <bool A_OC, bool B_OC, int BKP, int BN = 256>
 __device__ __forceinline__ W4Setup w4_setup(const GemmArgs& g) {
     W4Setup w;
     const int tid = threadIdx.x;
     w.lane = tid & 63;
     w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     w.wm0 = (w.wave >> 1) * 128;
-    w.wn0 = (w.wave & 1) * 128;
-    const BlockTile bt = map_block<256, 256>(g);
+    w.wn0 = (w.wave & 1) * (BN / 2);
+    const BlockTile bt = map_block<256, BN>(g);
     w.slice = bt.slice;
     w.m0 = bt.m0;
     w.n0 = bt.n0;
@@ -176,19 +176,25 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, smem + wave * (128 * 256));
 }
 
-// Placement of a 64-MFMA step's 16 fragment reads and NL loads (NL <= 16):
-// the index of the read (0..15) or load (0..NL-1) issued right after MFMA u,
-// or -1. With loads, one load after every fourth MFMA and the reads after the
-// two MFMAs that follow it; without loads, the reads after MFMAs 0..15.
-// (Measured and slower or equal: the reads first and the loads spread over
-// the rest; the loads first, one after every second MFMA; a load after every
-// third MFMA; a loadless step's reads after every second MFMA.)
+// Placement of the 8 + TN fragment reads and NL loads (NL <= 8 + TN) of one
+// 8 TN-MFMA step: the index of the read or load issued right after MFMA u, or
+// -1. The step's MFMAs form 16 groups of TN / 2. With loads, one load after
+// the first MFMA of a group and the reads after the next one or two MFMAs of
+// the first groups; without loads, the reads after MFMAs 0 .. 7 + TN. (For
+// TN = 8, measured and slower or equal: the reads first and the loads spread
+// over the rest; the loads first, one after every second MFMA; a load after
+// every third MFMA; a loadless step's reads after every second MFMA.)
+template <int TN>
 __device__ constexpr int w64_read_after(int nl, int u) {
-    if (nl == 0) return u < 16 ? u : -1;
-    return (u % 4 != 0 && u % 4 != 3 && u / 4 < 8) ? 2 * (u / 4) + (u % 4) - 1 : -1;
+    constexpr int gs = TN / 2, rpg = gs > 2 ? 2 : gs - 1, nr = 8 + TN;
+    if (nl == 0) return u < nr ? u : -1;
+    const int r = rpg * (u / gs) + (u % gs) - 1;
+    return (u % gs != 0 && u % gs <= rpg && r < nr) ? r : -1;
 }
+template <int TN>
 __device__ constexpr int w64_load_after(int nl, int u) {
-    return (nl > 0 && u % 4 == 0 && u / 4 < nl) ? u / 4 : -1;
+    constexpr int gs = TN / 2;
+    return (nl > 0 && u % gs == 0 && u / gs < nl) ? u / gs : -1;
 }
 
 // Orders every compiler write of the accumulators (their zero
@@ -196,23 +202,25 @@ __device__ constexpr int w64_load_after(int nl, int u) {
 // that read them: every accumulator passes through an empty asm (so such
 // writes must come before it), then a few wait states pass before the next
 // MFMA.
-__device__ __forceinline__ void w4_acc_fence(f32x4 (&acc)[8][8]) {
+template <int TN>
+__device__ __forceinline__ void w4_acc_fence(f32x4 (&acc)[8][TN]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
     asm volatile("s_nop 4" ::: "memory");
 }
 
 // The last MFMAs must have written their results before anything else
 // reads the accumulators: wait states, then every accumulator through an
 // empty asm (reads of them come after it).
-__device__ __forceinline__ void w4_acc_drain(f32x4 (&acc)[8][8]) {
+template <int TN>
+__device__ __forceinline__ void w4_acc_drain(f32x4 (&acc)[8][TN]) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
 // One v_mfma_f32_16x16x32_bf16 (B fragment as source A) whose accumulator is
@@ -220,41 +228,43 @@ __device__ __forceinline__ void w4_acc_drain(f32x4 (&acc)[8][8]) {
 // barriers is its place in the source. The compiler's register allocator
 // otherwise moves 256 accumulators between AGPRs and VGPRs when a step issues
 // many loads. Hazards the compiler no longer sees are covered by the kernel:
-// an accumulator is read again only by the same MFMA 64 MFMAs later, sources
+// an accumulator is read again only by the same MFMA 32 or more MFMAs later, sources
 // come from LDS reads the compiler waits for, and s_nops follow the zero
 // initialisation and precede the epilogue.
 __device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& b, const bf16x8& a) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
-template <bool A_OC, bool B_OC, bool OUT_F32>
+template <bool A_OC, bool B_OC, bool OUT_F32, int BN>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64_kernel(
     GemmArgs g) {
     constexpr int MF = 16, BKP = 64;
-    constexpr int kABytes = 256 * BKP * 2;                                       // 32 KB per operand
+    constexpr int TN = BN / 32;                                                  // 16-column blocks per wave
+    constexpr int kABytes = 256 * BKP * 2;                                       // 32 KB per operand tile
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;                                // 8
-    constexpr int kLoads = kLA + DmaPP<B_OC, BKP>::kInstr;                       // per wave per stage
+    constexpr int kLoads = kLA + DmaPP<B_OC, BKP, BN>::kInstr;                   // per wave per stage
     // one array per slot and operand: the compiler tracks each array's
     // direct-to-LDS writes separately, so an LDS read waits only for the
-    // loads into the array it reads
+    // loads into the array it reads. B tiles narrower than 256 rows keep
+    // 32 KB arrays: each array is one wave's epilogue staging space.
     __shared__ __attribute__((aligned(1024))) char a0[kABytes];
     __shared__ __attribute__((aligned(1024))) char b0[kABytes];
     __shared__ __attribute__((aligned(1024))) char a1[kABytes];
     __shared__ __attribute__((aligned(1024))) char b1[kABytes];
 
-    const W4Setup w = w4_setup<A_OC, B_OC, BKP>(g);
+    const W4Setup w = w4_setup<A_OC, B_OC, BKP, BN>(g);
     const int lane = w.lane, wave = w.wave, wm0 = w.wm0, wn0 = w.wn0, nkt = w.nkt;
     DmaPP<A_OC, BKP> da;
-    DmaPP<B_OC, BKP> db;
+    DmaPP<B_OC, BKP, BN> db;
     da.init(wave, lane, g.lda, w.m0, g.M);
     db.init(wave, lane, g.ldb, w.n0, g.N);
 
-    f32x4 acc[8][8];
+    f32x4 acc[8][TN];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    bf16x8 fa[2][8], fb[2][8];
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 fa[2][8], fb[2][TN];
 
     // byte offsets of stage SIDX along the reduction (past the end: the last stage)
 #define FCW64_STEPS(SIDX)                                                                  \
@@ -268,24 +278,24 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         da.issue_full(w.ra, SA, sa_, wave);              \
         db.issue_full(w.rb, SB, sb_, wave);              \
     }
-    // one 32-value step: 64 MFMAs from set CUR; after each of the first 16 the
-    // LDS read of one fragment of step KS of slot (RA, RB) into set NXT; then
-    // the loads LOADS selects (bit 0: operand A into LA, bit 1: operand B into
-    // LB) of stage LSTAGE, spread evenly over the remaining MFMAs
+    // one 32-value step: 8 TN MFMAs from set CUR, interleaved (w64_read_after,
+    // w64_load_after) with the LDS reads of the fragments of step KS of slot
+    // (RA, RB) into set NXT and the loads LOADS selects (bit 0: operand A into
+    // LA, bit 1: operand B into LB) of stage LSTAGE
 #define FCW64_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, LSTAGE)                                        \
     {                                                                                                  \
         FCW64_STEPS(LSTAGE)                                                                            \
         constexpr int la_ = ((LOADS) & 1) ? kLA : 0;                                                   \
         constexpr int nl_ = la_ + (((LOADS) & 2) ? kLoads - kLA : 0);                                  \
-        _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
-            mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
-            const int r_ = w64_read_after(nl_, u);                                              \
+        _Pragma("unroll") for (int u = 0; u < 8 * TN; ++u) {                                           \
+            mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], fa[CUR][u / TN]);                          \
+            const int r_ = w64_read_after<TN>(nl_, u);                                                 \
             if (r_ >= 0 && r_ < 8) {                                                                   \
                 fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
             } else if (r_ >= 8) {                                                                      \
-                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
+                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + (r_ - 8) * MF, KS, lane);   \
             }                                                                                          \
-            const int l_ = w64_load_after(nl_, u);                                             \
+            const int l_ = w64_load_after<TN>(nl_, u);                                                 \
             if (l_ >= 0 && l_ < la_)                                                                   \
                 da.issue_one(w.ra, LA, sa_, wave, l_);                                                 \
             else if (l_ >= la_)                                                                        \
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(a0, wm0 + i * MF, 0, lane);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF>(b0, wn0 + j * MF, 0, lane);
+        for (int j = 0; j < TN; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(b0, wn0 + j * MF, 0, lane);
         w4_acc_fence(acc);  // zeroed accumulators before the first MFMA reads them
         for (int t = 0; t < nkt; t += 2) {     // nkt is even: the reduction is a multiple of 128
             FCW64_STAGE(t, a0, b0, a1, b1)
@@ -347,32 +357,33 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 // that one loop: a stage count that is not a multiple of 6 is padded at the
 // front with virtual stages of zeros (up to five stages of extra MFMA work;
 // the tuner weighs it against gemm_w4k64_kernel).
-template <bool A_OC, bool B_OC, bool OUT_F32>
+template <bool A_OC, bool B_OC, bool OUT_F32, int BN>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
     GemmArgs g) {
     constexpr int MF = 16, BKP = 64;
-    constexpr int kT = 256 * BKP * 2;  // 32 KB per operand tile
+    constexpr int TN = BN / 32;        // 16-column blocks per wave
+    constexpr int kT = 256 * BKP * 2;  // 32 KB per tile array (also one wave's epilogue staging)
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
-    constexpr int kLB = DmaPP<B_OC, BKP>::kInstr;
+    constexpr int kLB = DmaPP<B_OC, BKP, BN>::kInstr;
     __shared__ __attribute__((aligned(1024))) char ta0[kT];
     __shared__ __attribute__((aligned(1024))) char ta1[kT];
     __shared__ __attribute__((aligned(1024))) char ta2[kT];
     __shared__ __attribute__((aligned(1024))) char tb0[kT];
     __shared__ __attribute__((aligned(1024))) char tb1[kT];
 
-    const W4Setup w = w4_setup<A_OC, B_OC, BKP>(g);
+    const W4Setup w = w4_setup<A_OC, B_OC, BKP, BN>(g);
     const int lane = w.lane, wave = w.wave, wm0 = w.wm0, wn0 = w.wn0, nkt = w.nkt;
     DmaPP<A_OC, BKP> da;
-    DmaPP<B_OC, BKP> db;
+    DmaPP<B_OC, BKP, BN> db;
     da.init(wave, lane, g.lda, w.m0, g.M);
     db.init(wave, lane, g.ldb, w.n0, g.N);
 
-    f32x4 acc[8][8];
+    f32x4 acc[8][TN];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    bf16x8 fa[2][8], fb[2][8];
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 fa[2][8], fb[2][TN];
 
 #define FCR_TA(I) ((I) == 0 ? ta0 : (I) == 1 ? ta1 : ta2)
 #define FCR_TB(I) ((I) == 0 ? tb0 : tb1)
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #define FCR_STEP_B(SIDX) (uint32_t)(B_OC ? FCR_OFF(SIDX) * g.ldb * 2 : FCR_OFF(SIDX) * 2)
 #define FCR_RA(SIDX) ((SIDX) < 0 ? rza : w.ra)
 #define FCR_RB(SIDX) ((SIDX) < 0 ? rzb : w.rb)
-    // 64 MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
+    // 8 TN MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
     // set NXT; with LOADS, the B tile of stage T + 2 into LB, then the A tile
     // of stage T + 3 into LA, placed as w64_read_after / w64_load_after say
 #define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, T)                                              \
@@ -389,15 +400,15 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         const uint32_t sb_ = FCR_STEP_B((T) + 2), sa_ = FCR_STEP_A((T) + 3);                           \
         const __amdgpu_buffer_rsrc_t rb_ = FCR_RB((T) + 2), ra_ = FCR_RA((T) + 3);                     \
         constexpr int nl_ = (LOADS) ? kLA + kLB : 0;                                                   \
-        _Pragma("unroll") for (int u = 0; u < 64; ++u) {                                               \
-            mfma_agpr(acc[u >> 3][u & 7], fb[CUR][u & 7], fa[CUR][u >> 3]);                            \
-            const int r_ = w64_read_after(nl_, u);                                             \
+        _Pragma("unroll") for (int u = 0; u < 8 * TN; ++u) {                                           \
+            mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], fa[CUR][u / TN]);                          \
+            const int r_ = w64_read_after<TN>(nl_, u);                                                 \
             if (r_ >= 0 && r_ < 8) {                                                                   \
                 fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
             } else if (r_ >= 8) {                                                                      \
-                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF>(RB, wn0 + (r_ - 8) * MF, KS, lane);       \
+                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + (r_ - 8) * MF, KS, lane);   \
             }                                                                                          \
-            const int l_ = w64_load_after(nl_, u);                                             \
+            const int l_ = w64_load_after<TN>(nl_, u);                                                 \
             if (l_ >= 0 && l_ < kLB)                                                                   \
                 db.issue_one(rb_, LB, sb_, wave, l_);                                                  \
             else if (l_ >= kLB)                                                                        \
@@ -434,7 +445,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF>(tb0, wn0 + j * MF, 0, lane);
+        for (int j = 0; j < TN; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(tb0, wn0 + j * MF, 0, lane);
         w4_acc_fence(acc);
         for (int t = -pad; t < nkt; t += 6) {  // nkt + pad is a multiple of 6
             FCR_STAGE(0, t)
@@ -470,10 +481,12 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // instance the table below names.
-#define FCW4_INST(AOC, BOC, F32)                                          \
-    template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);     \
-    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32>(GemmArgs);  \
-    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32>(GemmArgs);
+#define FCW4_INST(AOC, BOC, F32)                                               \
+    template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);          \
+    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32, 256>(GemmArgs);  \
+    template __global__ void gemm_w4k64_kernel<AOC, BOC, F32, 192>(GemmArgs);  \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 256>(GemmArgs);  \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 192>(GemmArgs);
 FCW4_INST(false, false, false)
 FCW4_INST(false, true, false)
 FCW4_INST(true, false, false)
@@ -492,31 +505,42 @@ struct W4Entry {
 
 #define FCW4_K(KN, AOC, BOC, F32) \
     W4Entry { KN<AOC, BOC, F32>, #KN "<" #AOC ", " #BOC ", " #F32 ">" }
-#define FCW4_ALL(KN)                                                                               \
-    FCW4_K(KN, false, false, false), FCW4_K(KN, false, true, false), FCW4_K(KN, true, false, false), \
-        FCW4_K(KN, true, true, false), FCW4_K(KN, false, false, true), FCW4_K(KN, false, true, true), \
-        FCW4_K(KN, true, false, true), FCW4_K(KN, true, true, true)
-// [variant][out_f32][a_oc][b_oc]
-const W4Entry kW4[3][8] = {{FCW4_ALL(gemm_w4_kernel)}, {FCW4_ALL(gemm_w4k64_kernel)},
-                           {FCW4_ALL(gemm_w4k64r_kernel)}};
+#define FCW4_2S(BN, AOC, BOC, F32) \
+    W4Entry { gemm_w4k64_kernel<AOC, BOC, F32, BN>, "gemm_w4k64_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ">" }
+#define FCW4_RING(BN, AOC, BOC, F32) \
+    W4Entry { gemm_w4k64r_kernel<AOC, BOC, F32, BN>, "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ">" }
+#define FCW4_ALL(K, X)                                                                   \
+    K(X, false, false, false), K(X, false, true, false), K(X, true, false, false),       \
+        K(X, true, true, false), K(X, false, false, true), K(X, false, true, true),      \
+        K(X, true, false, true), K(X, true, true, true)
+// [kernel][out_f32][a_oc][b_oc]: the 32-value-stage kernel; the two-slot and
+// the ring kernel, each with 256- and 192-column block tiles
+const W4Entry kW4[5][8] = {{FCW4_ALL(FCW4_K, gemm_w4_kernel)}, {FCW4_ALL(FCW4_2S, 256)}, {FCW4_ALL(FCW4_2S, 192)},
+                           {FCW4_ALL(FCW4_RING, 256)},         {FCW4_ALL(FCW4_RING, 192)}};
 
-const W4Entry& w4_entry(int variant, bool a_oc, bool b_oc, bool out_f32) {
-    return kW4[variant < 0 || variant > 2 ? 0 : variant][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
+int w4_row(int variant, int bn) {
+    if (variant == 0) return 0;
+    return (variant == 1 ? 1 : 3) + (bn == 192 ? 1 : 0);
+}
+
+const W4Entry& w4_entry(int variant, int bn, bool a_oc, bool b_oc, bool out_f32) {
+    return kW4[w4_row(variant, bn)][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
 }
 
 }  // namespace
 
-const char* w4_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32) {
-    return w4_entry(variant, a_oc, b_oc, out_f32).name;
+const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32) {
+    return w4_entry(variant, bn, a_oc, b_oc, out_f32).name;
 }
 
-hipError_t launch_gemm_w4(int variant, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
+hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream) {
-    const int64_t blocks = ((args.M + 255) / 256) * ((args.N + 255) / 256) * (int64_t)args.splits;
+    if (bn != 256 && (variant == 0 || bn != 192)) return hipErrorInvalidValue;
+    const int64_t blocks = ((args.M + 255) / 256) * ((args.N + bn - 1) / bn) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(w4_entry(variant, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks), dim3(kW4Threads), 0, stream,
-                       args);
+    hipLaunchKernelGGL(w4_entry(variant, bn, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks), dim3(kW4Threads), 0,
+                       stream, args);
     return hipGetLastError();
 }
 

@@ -143,9 +143,12 @@ def test_exact_power_of_two_scaled_inputs():
 # ragged output tiles and two- and four-way reduction splits. (384, 1024, 384):
 # every reduction a multiple of 128 (64-value stages in pairs), ragged tiles.
 # (352, 608, 224): every reduction length is 32 more than a multiple of 64;
-# split slices of 320 + 288 and of 192 + 192 + 192 + 32.
+# split slices of 320 + 288 and of 192 + 192 + 192 + 32. (384, 1024, 328):
+# forward and backward-weight outputs ragged against the 256- and 192-column
+# block tiles (328 = 192 + 136), the second wave column of a 192-column tile
+# partly outside the matrix.
 @pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192),
-                                   (384, 1024, 384), (352, 608, 224)],
+                                   (384, 1024, 384), (352, 608, 224), (384, 1024, 328)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
