@@ -415,7 +415,7 @@ std::string describe(const Problem& p, int id) {
                          (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
     const bool f32 = slices > 1 ? true : p.out_f32;
     const char* kname = pl.family == 0            ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
-                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, w4_bn(pl), q.a_oc, q.b_oc, f32)
+                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, w4_bn(pl), q.a_oc, q.b_oc, f32, p.K, ks, slices)
                         : pl.family >= 2          ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
                                          : gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc, f32,
                                                             aligned);

@@ -64,10 +64,16 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 // variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
 // 2 slots (whole-cache-line rows for reduction-contiguous operands); 2: the
 // same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about
-// two stages to land. bn is 256, or 192 for variants 1 and 2.
+// two stages to land. bn is 256, or 192 for variants 1 and 2. The ring runs
+// its reduction in periods of 6 stages; when every slice's stage count mod
+// 6 is 2 or 4 it starts with that many straight-line stages (the last
+// positions of a period), else it pads the front with zero stages.
 hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream);
-const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32);
+// (K, k_split, splits: the reduction slicing, which picks the ring kernel's
+// head form)
+const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, int64_t K, int64_t k_split,
+                           int splits);
 
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

@@ -40,6 +40,8 @@
 // is two 32-value steps; the barrier sits before the second: it certifies
 // stage t + 1 (whose first step the wave reads next) and frees stage t's
 // slot for the loads of stage t + 2, which have two steps to land.
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace fcs {
@@ -354,10 +356,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 // tile), so A loads have three steps to land and B loads at least one and a
 // half. The loop body holds one period of six stages with every tile fixed
 // (stage t in A tile t mod 3 and B tile t mod 2), and the control flow stays
-// that one loop: a stage count that is not a multiple of 6 is padded at the
-// front with virtual stages of zeros (up to five stages of extra MFMA work;
-// the tuner weighs it against gemm_w4k64_kernel).
-template <bool A_OC, bool B_OC, bool OUT_F32, int BN>
+// that one loop. A stage count that is not a multiple of 6 either
+// (HEAD < 0) is padded at the front with virtual stages of zeros (up to five
+// stages of extra MFMA work; the tuner weighs it against gemm_w4k64_kernel)
+// or (HEAD = 1 .. 5, the stage count mod 6, the same for every block) starts
+// with HEAD straight-line stages that take the last HEAD positions of a
+// period: the padded schedule without its virtual stages, no extra work, and
+// still one control path.
+template <bool A_OC, bool B_OC, bool OUT_F32, int BN, int HEAD>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
     GemmArgs g) {
     constexpr int MF = 16, BKP = 64;
@@ -428,32 +434,71 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     }
 
     if (nkt > 0) {
-        // The loop runs whole periods of six stages: pad virtual stages
-        // -pad .. -1 go first and load through zero-size descriptors, so
-        // their tiles hold zeros and their MFMAs add nothing.
-        const int pad = (6 - nkt % 6) % 6;
         const __amdgpu_buffer_rsrc_t rza = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, 0, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rzb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, 0, 0, kRsrcWord3);
-        // stages -pad, -pad + 1 and the A tile of -pad + 2; wait for the first; read its step 0
-        da.issue_full(FCR_RA(-pad), ta0, FCR_STEP_A(-pad), wave);
-        db.issue_full(FCR_RB(-pad), tb0, FCR_STEP_B(-pad), wave);
-        da.issue_full(FCR_RA(1 - pad), ta1, FCR_STEP_A(1 - pad), wave);
-        db.issue_full(FCR_RB(1 - pad), tb1, FCR_STEP_B(1 - pad), wave);
-        da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
-        waitcnt<2 * kLA + kLB, 0>();
-        __builtin_amdgcn_s_barrier();
+        if constexpr (HEAD < 0) {
+            // The loop runs whole periods of six stages: pad virtual stages
+            // -pad .. -1 go first and load through zero-size descriptors, so
+            // their tiles hold zeros and their MFMAs add nothing.
+            const int pad = (6 - nkt % 6) % 6;
+            // stages -pad, -pad + 1 and the A tile of -pad + 2; wait for the first; read its step 0
+            da.issue_full(FCR_RA(-pad), ta0, FCR_STEP_A(-pad), wave);
+            db.issue_full(FCR_RB(-pad), tb0, FCR_STEP_B(-pad), wave);
+            da.issue_full(FCR_RA(1 - pad), ta1, FCR_STEP_A(1 - pad), wave);
+            db.issue_full(FCR_RB(1 - pad), tb1, FCR_STEP_B(1 - pad), wave);
+            da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
+            waitcnt<2 * kLA + kLB, 0>();
+            __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
+            for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(tb0, wn0 + j * MF, 0, lane);
-        w4_acc_fence(acc);
-        for (int t = -pad; t < nkt; t += 6) {  // nkt + pad is a multiple of 6
-            FCR_STAGE(0, t)
-            FCR_STAGE(1, t + 1)
-            FCR_STAGE(2, t + 2)
-            FCR_STAGE(3, t + 3)
-            FCR_STAGE(4, t + 4)
-            FCR_STAGE(5, t + 5)
+            for (int j = 0; j < TN; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(tb0, wn0 + j * MF, 0, lane);
+            w4_acc_fence(acc);
+            for (int t = -pad; t < nkt; t += 6) {  // nkt + pad is a multiple of 6
+                FCR_STAGE(0, t)
+                FCR_STAGE(1, t + 1)
+                FCR_STAGE(2, t + 2)
+                FCR_STAGE(3, t + 3)
+                FCR_STAGE(4, t + 4)
+                FCR_STAGE(5, t + 5)
+            }
+        } else {
+            // stages 0 .. HEAD - 1 take period positions P0 .. 5; stages 0, 1
+            // and the A tile of stage 2 go to those positions' tiles
+            constexpr int P0 = 6 - HEAD;
+            da.issue_full(w.ra, FCR_TA(P0 % 3), FCR_STEP_A(0), wave);
+            db.issue_full(w.rb, FCR_TB(P0 % 2), FCR_STEP_B(0), wave);
+            da.issue_full(w.ra, FCR_TA((P0 + 1) % 3), FCR_STEP_A(1), wave);
+            db.issue_full(w.rb, FCR_TB((P0 + 1) % 2), FCR_STEP_B(1), wave);
+            da.issue_full(w.ra, FCR_TA((P0 + 2) % 3), FCR_STEP_A(2), wave);
+            waitcnt<2 * kLA + kLB, 0>();
+            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                fa[0][i] = fragment_mf<A_OC, BKP, MF>(FCR_TA(P0 % 3), wm0 + i * MF, 0, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(FCR_TB(P0 % 2), wn0 + j * MF, 0, lane);
+            w4_acc_fence(acc);
+            if constexpr (HEAD >= 5) FCR_STAGE(1, HEAD - 5)
+            if constexpr (HEAD >= 4) FCR_STAGE(2, HEAD - 4)
+            if constexpr (HEAD >= 3) FCR_STAGE(3, HEAD - 3)
+            if constexpr (HEAD >= 2) FCR_STAGE(4, HEAD - 2)
+            if constexpr (HEAD >= 1) FCR_STAGE(5, HEAD - 1)
+            // nkt - HEAD is a positive multiple of 6 (the launcher picks this
+            // form only then). A do-while: with a path around the loop the
+            // compiler merges two sets of accumulators at its exit and may copy
+            // the last MFMA's result before that MFMA has written it.
+            int t = HEAD;
+            do {
+                FCR_STAGE(0, t)
+                FCR_STAGE(1, t + 1)
+                FCR_STAGE(2, t + 2)
+                FCR_STAGE(3, t + 3)
+                FCR_STAGE(4, t + 4)
+                FCR_STAGE(5, t + 5)
+                t += 6;
+            } while (t < nkt);
         }
         waitcnt<0, 0>();  // drain the trailing prefetches
     }
@@ -480,13 +525,23 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCW4_MFMA_STEP
 
 // Explicit instantiations: the host pass must emit a launch stub for every
-// instance the table below names.
+// instance the table below names. (The ring kernel's head forms with both
+// operands output-contiguous at 256 columns are not built: they spill.)
+#define FCW4_HINST(AOC, BOC, F32, BN)                                          \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, BN, 2>(GemmArgs); \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, BN, 4>(GemmArgs);
+#define FCW4_HINST_256_false_false(F32) FCW4_HINST(false, false, F32, 256)
+#define FCW4_HINST_256_false_true(F32) FCW4_HINST(false, true, F32, 256)
+#define FCW4_HINST_256_true_false(F32) FCW4_HINST(true, false, F32, 256)
+#define FCW4_HINST_256_true_true(F32)
 #define FCW4_INST(AOC, BOC, F32)                                               \
     template __global__ void gemm_w4_kernel<AOC, BOC, F32>(GemmArgs);          \
     template __global__ void gemm_w4k64_kernel<AOC, BOC, F32, 256>(GemmArgs);  \
     template __global__ void gemm_w4k64_kernel<AOC, BOC, F32, 192>(GemmArgs);  \
-    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 256>(GemmArgs);  \
-    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 192>(GemmArgs);
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 256, -1>(GemmArgs);  \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, 192, -1>(GemmArgs);  \
+    FCW4_HINST(AOC, BOC, F32, 192)                                                   \
+    FCW4_HINST_256_##AOC##_##BOC(F32)
 FCW4_INST(false, false, false)
 FCW4_INST(false, true, false)
 FCW4_INST(true, false, false)
@@ -496,6 +551,11 @@ FCW4_INST(false, true, true)
 FCW4_INST(true, false, true)
 FCW4_INST(true, true, true)
 #undef FCW4_INST
+#undef FCW4_HINST
+#undef FCW4_HINST_256_false_false
+#undef FCW4_HINST_256_false_true
+#undef FCW4_HINST_256_true_false
+#undef FCW4_HINST_256_true_true
 
 using KernelFn = void (*)(GemmArgs);
 struct W4Entry {
@@ -507,30 +567,72 @@ struct W4Entry {
     W4Entry { KN<AOC, BOC, F32>, #KN "<" #AOC ", " #BOC ", " #F32 ">" }
 #define FCW4_2S(BN, AOC, BOC, F32) \
     W4Entry { gemm_w4k64_kernel<AOC, BOC, F32, BN>, "gemm_w4k64_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ">" }
-#define FCW4_RING(BN, AOC, BOC, F32) \
-    W4Entry { gemm_w4k64r_kernel<AOC, BOC, F32, BN>, "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ">" }
+// the ring kernel with head HEAD, or the padded one where no head form is built
+template <bool AOC, bool BOC, bool F32, int BN, int HEAD>
+constexpr KernelFn ring_fn() {
+    if constexpr (HEAD > 0 && AOC && BOC && BN == 256)
+        return gemm_w4k64r_kernel<AOC, BOC, F32, BN, -1>;
+    else
+        return gemm_w4k64r_kernel<AOC, BOC, F32, BN, HEAD>;
+}
+#define FCW4_R(BN, TL, AOC, BOC, F32)                                                                  \
+    W4Entry {                                                                                          \
+        ring_fn<AOC, BOC, F32, BN, TL>(),                                                              \
+            (TL > 0 && AOC && BOC && BN == 256)                                                        \
+                ? "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ", -1>"                      \
+                : "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " #BN ", " #TL ">"                 \
+    }
+#define FCW4_RING_P(BN, AOC, BOC, F32) FCW4_R(BN, -1, AOC, BOC, F32)
+#define FCW4_RING_H2(BN, AOC, BOC, F32) FCW4_R(BN, 2, AOC, BOC, F32)
+#define FCW4_RING_H4(BN, AOC, BOC, F32) FCW4_R(BN, 4, AOC, BOC, F32)
 #define FCW4_ALL(K, X)                                                                   \
     K(X, false, false, false), K(X, false, true, false), K(X, true, false, false),       \
         K(X, true, true, false), K(X, false, false, true), K(X, false, true, true),      \
         K(X, true, false, true), K(X, true, true, true)
-// [kernel][out_f32][a_oc][b_oc]: the 32-value-stage kernel; the two-slot and
-// the ring kernel, each with 256- and 192-column block tiles
-const W4Entry kW4[5][8] = {{FCW4_ALL(FCW4_K, gemm_w4_kernel)}, {FCW4_ALL(FCW4_2S, 256)}, {FCW4_ALL(FCW4_2S, 192)},
-                           {FCW4_ALL(FCW4_RING, 256)},         {FCW4_ALL(FCW4_RING, 192)}};
+// [kernel][out_f32][a_oc][b_oc]: the 32-value-stage kernel; the two-slot
+// kernel with 256- and 192-column block tiles; the ring kernel with 256- and
+// 192-column tiles, each padded at the front or starting with a head of 2 or
+// 4 stages
+const W4Entry kW4[9][8] = {{FCW4_ALL(FCW4_K, gemm_w4_kernel)},
+                           {FCW4_ALL(FCW4_2S, 256)},
+                           {FCW4_ALL(FCW4_2S, 192)},
+                           {FCW4_ALL(FCW4_RING_P, 256)},
+                           {FCW4_ALL(FCW4_RING_P, 192)},
+                           {FCW4_ALL(FCW4_RING_H2, 256)},
+                           {FCW4_ALL(FCW4_RING_H2, 192)},
+                           {FCW4_ALL(FCW4_RING_H4, 256)},
+                           {FCW4_ALL(FCW4_RING_H4, 192)}};
 
-int w4_row(int variant, int bn) {
+int w4_row(int variant, int bn, int head) {
     if (variant == 0) return 0;
-    return (variant == 1 ? 1 : 3) + (bn == 192 ? 1 : 0);
+    if (variant == 1) return bn == 192 ? 2 : 1;
+    return (head == 2 ? 5 : head == 4 ? 7 : 3) + (bn == 192 ? 1 : 0);
 }
 
-const W4Entry& w4_entry(int variant, int bn, bool a_oc, bool b_oc, bool out_f32) {
-    return kW4[w4_row(variant, bn)][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
+// The ring kernel's head for this launch: the reduction slices' stage count
+// mod 6 when it is 2 or 4 for every slice and every slice has a whole period
+// after its head, else -1 (pad at the front).
+// (Both operands output-contiguous at 256 columns keep the padded form: with
+// a head, that kernel runs out of registers and spills in its main loop.)
+int ring_head(int64_t K, int64_t k_split, int splits, int bn, bool a_oc, bool b_oc) {
+    if (bn == 256 && a_oc && b_oc) return -1;
+    const int64_t first = (std::min(k_split, K) + 63) / 64;
+    const int64_t last = (K - (int64_t)(splits - 1) * k_split + 63) / 64;
+    const int r = (int)(first % 6);
+    return (r == 2 || r == 4) && last % 6 == r && std::min(first, last) > 6 ? r : -1;
+}
+
+const W4Entry& w4_entry(int variant, int bn, int head, bool a_oc, bool b_oc, bool out_f32) {
+    return kW4[w4_row(variant, bn, head)][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
 }
 
 }  // namespace
 
-const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32) {
-    return w4_entry(variant, bn, a_oc, b_oc, out_f32).name;
+const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, int64_t K, int64_t k_split,
+                           int splits) {
+    return w4_entry(variant, bn, variant == 2 ? ring_head(K, k_split, splits, bn, a_oc, b_oc) : -1, a_oc, b_oc,
+                    out_f32)
+        .name;
 }
 
 hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
@@ -539,8 +641,9 @@ hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f3
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + bn - 1) / bn) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(w4_entry(variant, bn, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks), dim3(kW4Threads), 0,
-                       stream, args);
+    const int head = variant == 2 ? ring_head(args.K, args.k_split, args.splits, bn, a_oc, b_oc) : -1;
+    hipLaunchKernelGGL(w4_entry(variant, bn, head, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks),
+                       dim3(kW4Threads), 0, stream, args);
     return hipGetLastError();
 }
 

@@ -146,9 +146,12 @@ def test_exact_power_of_two_scaled_inputs():
 # split slices of 320 + 288 and of 192 + 192 + 192 + 32. (384, 1024, 328):
 # forward and backward-weight outputs ragged against the 256- and 192-column
 # block tiles (328 = 192 + 136), the second wave column of a 192-column tile
-# partly outside the matrix.
+# partly outside the matrix. (512, 640, 1024): the ring kernel's head forms
+# (reductions of 6 q + 2 or 6 q + 4 64-value stages, q >= 1) in all three
+# products: 10 stages (head of 4) forward, 16 (4) backward-data, 8 (2)
+# backward-weight, and the split slices of 8 + 8 (2) and 4 x 4 (padded).
 @pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192),
-                                   (384, 1024, 384), (352, 608, 224), (384, 1024, 328)],
+                                   (384, 1024, 384), (352, 608, 224), (384, 1024, 328), (512, 640, 1024)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
