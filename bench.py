@@ -34,9 +34,8 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "sharded_fc_layer_amd", "csrc", f)
-                  for f in ("gemm_common.h", "gemm_pipe.hip", "gemm_w4.hip", "gemm_bf16.hip", "aux_kernels.hip",
-                            "fcshard_api.hip")]
+CSRC = os.path.join(ROOT, "sharded_fc_layer_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
 
 
 def kernel_source_hash() -> str:

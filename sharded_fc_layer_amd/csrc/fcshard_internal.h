@@ -75,6 +75,22 @@ hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f3
 const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, int64_t K, int64_t k_split,
                            int splits);
 
+// One kernel instance and its name as profilers show it.
+struct W4Kernel {
+    void (*fn)(GemmArgs);
+    const char* name;
+};
+
+// The ring kernel (variant 2 above) for block-tile width BN (256 or 192):
+// head = 2 or 4 picks the head form, anything else the padded one. Defined
+// in gemm_w4_ring256.hip and gemm_w4_ring192.hip.
+template <int BN>
+W4Kernel w4_ring_kernel(int head, bool a_oc, bool b_oc, bool out_f32);
+template <>
+W4Kernel w4_ring_kernel<256>(int head, bool a_oc, bool b_oc, bool out_f32);
+template <>
+W4Kernel w4_ring_kernel<192>(int head, bool a_oc, bool b_oc, bool out_f32);
+
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                  hipStream_t stream);
