@@ -390,7 +390,7 @@ fc_status grow_workspace(int dev, int64_t bytes) {
     DevState& d = g_dev[dev];
     if (bytes <= d.ws_bytes) return FC_OK;
     if (hipDeviceSynchronize() != hipSuccess) return FC_E_HIP;  // old workspace may be in use
-    if (d.ws) hipFree(d.ws);
+    if (d.ws) (void)hipFree(d.ws);
     d.ws = nullptr;
     d.ws_bytes = 0;
     if (hipMalloc(&d.ws, (size_t)bytes) != hipSuccess) {
@@ -435,10 +435,10 @@ struct TuneBuffers {
     void* dY = nullptr;
     void* out = nullptr;
     ~TuneBuffers() {
-        if (X) hipFree(X);
-        if (W) hipFree(W);
-        if (dY) hipFree(dY);
-        if (out) hipFree(out);
+        if (X) (void)hipFree(X);
+        if (W) (void)hipFree(W);
+        if (dY) (void)hipFree(dY);
+        if (out) (void)hipFree(out);
     }
 };
 
@@ -459,8 +459,8 @@ struct CacheFlush {
     }
     hipError_t run(hipStream_t s) const { return launch_transpose_bf16(a, b, kRows, kCols, s); }
     ~CacheFlush() {
-        if (a) hipFree(a);
-        if (b) hipFree(b);
+        if (a) (void)hipFree(a);
+        if (b) (void)hipFree(b);
     }
 };
 
@@ -474,12 +474,12 @@ float time_plan(const Problem& p, const Plan& pl, void* ws, hipStream_t s, int w
     std::vector<float> t;
     for (int i = 0; i < reps && *ok; ++i) {
         if (flush && flush->run(s) != hipSuccess) *ok = false;
-        hipEventRecord(ev[0], s);
+        if (hipEventRecord(ev[0], s) != hipSuccess) *ok = false;
         if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
-        hipEventRecord(ev[1], s);
+        if (hipEventRecord(ev[1], s) != hipSuccess) *ok = false;
         if (hipEventSynchronize(ev[1]) != hipSuccess) *ok = false;
         float ms = 0;
-        hipEventElapsedTime(&ms, ev[0], ev[1]);
+        if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) *ok = false;
         t.push_back(ms);
     }
     if (!*ok || t.empty()) return 1e30f;
@@ -600,7 +600,11 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         return FC_E_HIP;
     }
     hipEvent_t ev[2];
-    if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) return FC_E_HIP;
+    if (hipEventCreate(&ev[0]) != hipSuccess) return FC_E_HIP;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return FC_E_HIP;
+    }
     const bool exhaustive = (flags & 1) != 0;
     const int warm = exhaustive ? 3 : 2, reps = exhaustive ? 10 : 5;
     CacheFlush flush_bufs;
@@ -687,8 +691,8 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
             g_plans[make_key(dev, op, M, K, N, x_order, w_order, out_dtype)] = PlanEntry{pick, pick_ms};
         }
     }
-    hipEventDestroy(ev[0]);
-    hipEventDestroy(ev[1]);
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
     if (hipStreamSynchronize(s) != hipSuccess) result = FC_E_HIP;
     return result;
 }
@@ -772,10 +776,10 @@ fc_status fc_release(void) {
             int cur = 0;
             if (hipGetDevice(&cur) != hipSuccess) return FC_E_HIP;
             if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) st = FC_E_HIP;
-            hipFree(g_dev[d].ws);
+            (void)hipFree(g_dev[d].ws);
             g_dev[d].ws = nullptr;
             g_dev[d].ws_bytes = 0;
-            hipSetDevice(cur);
+            (void)hipSetDevice(cur);
         }
     }
     return st;
