@@ -35,7 +35,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "sharded_fc_layer_amd", "csrc")
-KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+# every source with device code (the C-ABI layer, fcshard_api.hip, is host code only)
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                        if f.endswith((".hip", ".h")) and f != "fcshard_api.hip")
 
 
 def kernel_source_hash() -> str:
