@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kW4Threads = 256;
 
-// block set-up shared by both kernels
+// block set-up shared by the kernels
 struct W4Setup {
     int lane, wave, wm0, wn0, slice, nkt;
     int64_t m0, n0, kbeg, kend;

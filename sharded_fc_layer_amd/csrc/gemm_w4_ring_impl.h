@@ -23,10 +23,11 @@ namespace {
 // that one loop. A stage count that is not a multiple of 6 either
 // (HEAD < 0) is padded at the front with virtual stages of zeros (up to five
 // stages of extra MFMA work; the tuner weighs it against gemm_w4k64_kernel)
-// or (HEAD = 1 .. 5, the stage count mod 6, the same for every block) starts
-// with HEAD straight-line stages that take the last HEAD positions of a
-// period: the padded schedule without its virtual stages, no extra work, and
-// still one control path.
+// or (HEAD = the stage count mod 6, the same for every block, with at least
+// one whole period after it; 2 and 4 are built) starts with HEAD
+// straight-line stages that take the last HEAD positions of a period, then
+// runs the periods as a do-while: the padded schedule without its virtual
+// stages, no extra work, and still one control path.
 template <bool A_OC, bool B_OC, bool OUT_F32, int BN, int HEAD>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
     GemmArgs g) {
