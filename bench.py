@@ -40,13 +40,18 @@ KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                         if f.endswith((".hip", ".h")) and f != "fcshard_api.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; counter figures taken on other sources are stale."""
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the device code (comments and whitespace removed): counter figures
+    taken on other code are stale; comment edits leave them valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(sources or KERNEL_SOURCES):
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.basename(f).encode() + b"\0" + " ".join(text.split()).encode() + b"\0")
     return h.hexdigest()[:16]
 
 
