@@ -40,10 +40,11 @@ constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
 // 6-8: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
 // 32-value stages (6), 64-value stages in two LDS slots (7) or in a ring of
-// three A and two B tiles (8). Families 7 and 8 also run 256 x 192 block
-// tiles (tile 2; 128 x 96 per wave): where 256 x 256 tiles leave CUs idle
-// (192 tiles on 256 CUs), 256 x 192 ones may fill them (256 tiles).
-constexpr int kNumFamilies = 9;
+// three A and two B tiles (8), or in the mirrored ring of two A and three B
+// tiles (9). Families 7 and 8 also run 256 x 192 block tiles (tile 2;
+// 128 x 96 per wave): where 256 x 256 tiles leave CUs idle (192 tiles on 256
+// CUs), 256 x 192 ones may fill them (256 tiles).
+constexpr int kNumFamilies = 10;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
@@ -53,7 +54,7 @@ struct Plan {
     int tile;
     int split;   // number of reduction slices requested
     int copy;    // bit mask
-    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-8 one wave per SIMD
+    int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-9 one wave per SIMD
 };
 
 Plan decode_plan(int id) {
@@ -70,7 +71,9 @@ int encode_plan(int tile, int split_idx, int copy, int family) {
 }
 
 // block-tile width (output columns) of a one-wave-per-SIMD plan
-int w4_bn(const Plan& pl) { return pl.family > kFamilyW4 && pl.tile == 2 ? 192 : 256; }
+int w4_bn(const Plan& pl) {
+    return (pl.family == kFamilyW4 + 1 || pl.family == kFamilyW4 + 2) && pl.tile == 2 ? 192 : 256;
+}
 
 // One GEMM in kernel terms, resolved from an ABI call.
 struct Problem {
@@ -136,7 +139,7 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 1) || (uintptr_t)p.A % 16 == 0) &&
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
-    if (pl.family >= 2 && pl.tile != 0 && !(pl.family > kFamilyW4 && pl.tile == 2)) return false;
+    if (pl.family >= 2 && pl.tile != 0 && !(w4_bn(pl) == 192)) return false;
     if (pl.family >= kFamilyW4) {  // whole stages (pairs of 32- or 64-value stages for 6 and 7)
         const int64_t q = pl.family == kFamilyW4 ? 64 : pl.family == kFamilyW4 + 1 ? 128 : 64;
         int64_t ks;

@@ -279,11 +279,9 @@ const W4Kernel kW4[3][8] = {{FCW4_ALL(FCW4_K, gemm_w4_kernel)}, {FCW4_ALL(FCW4_2
 
 // The ring kernel's head for this launch: the reduction slices' stage count
 // mod 6 when it is 2 or 4 for every slice and every slice has a whole period
-// after its head, else -1 (pad at the front). (Both operands
-// output-contiguous at 256 columns always run the padded form: with a head,
-// that kernel runs out of registers and spills in its main loop.)
-int ring_head(int64_t K, int64_t k_split, int splits, int bn, bool a_oc, bool b_oc) {
-    if (bn == 256 && a_oc && b_oc) return -1;
+// after its head, else -1 (pad at the front). The kernel tables map head
+// forms that are not built (they would spill) to the padded form.
+int ring_head(int64_t K, int64_t k_split, int splits) {
     const int64_t first = (std::min(k_split, K) + 63) / 64;
     const int64_t last = (K - (int64_t)(splits - 1) * k_split + 63) / 64;
     const int r = (int)(first % 6);
@@ -292,8 +290,9 @@ int ring_head(int64_t K, int64_t k_split, int splits, int bn, bool a_oc, bool b_
 
 W4Kernel w4_entry(int variant, int bn, int head, bool a_oc, bool b_oc, bool out_f32) {
     if (variant == 2)
-        return bn == 192 ? w4_ring_kernel<192>(head, a_oc, b_oc, out_f32)
-                         : w4_ring_kernel<256>(head, a_oc, b_oc, out_f32);
+        return bn == 192 ? w4_ring_kernel<192, 3>(head, a_oc, b_oc, out_f32)
+                         : w4_ring_kernel<256, 3>(head, a_oc, b_oc, out_f32);
+    if (variant == 3) return w4_ring_kernel<256, 2>(head, a_oc, b_oc, out_f32);
     const int row = variant == 0 ? 0 : bn == 192 ? 2 : 1;
     return kW4[row][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
 }
@@ -302,19 +301,17 @@ W4Kernel w4_entry(int variant, int bn, int head, bool a_oc, bool b_oc, bool out_
 
 const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, int64_t K, int64_t k_split,
                            int splits) {
-    return w4_entry(variant, bn, variant == 2 ? ring_head(K, k_split, splits, bn, a_oc, b_oc) : -1, a_oc, b_oc,
-                    out_f32)
-        .name;
+    return w4_entry(variant, bn, variant >= 2 ? ring_head(K, k_split, splits) : -1, a_oc, b_oc, out_f32).name;
 }
 
 hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream) {
-    if (variant < 0 || variant > 2) return hipErrorInvalidValue;
-    if (bn != 256 && (variant == 0 || bn != 192)) return hipErrorInvalidValue;
+    if (variant < 0 || variant > 3) return hipErrorInvalidValue;
+    if (bn != 256 && (variant == 0 || variant == 3 || bn != 192)) return hipErrorInvalidValue;
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + bn - 1) / bn) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int head = variant == 2 ? ring_head(args.K, args.k_split, args.splits, bn, a_oc, b_oc) : -1;
+    const int head = variant >= 2 ? ring_head(args.K, args.k_split, args.splits) : -1;
     hipLaunchKernelGGL(w4_entry(variant, bn, head, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks),
                        dim3(kW4Threads), 0, stream, args);
     return hipGetLastError();

@@ -1,12 +1,16 @@
 // The ring kernel (gemm_w4k64r_kernel) and its instances for one block-tile
-// width, FCW4_RING_BN (256 or 192), set by the including source file; each
-// width is its own translation unit so that the build compiles them in
+// width, FCW4_RING_BN (256 or 192), and one split of the five LDS tiles,
+// FCW4_RING_NA A tiles (3 unless set), set by the including source file; each
+// such pair is its own translation unit so that the build compiles them in
 // parallel. Requirements as in gemm_w4.hip (K and split slices multiples of
 // 64).
 #include "gemm_w4_common.h"
 
 #ifndef FCW4_RING_BN
 #error "FCW4_RING_BN must be defined (256 or 192)"
+#endif
+#ifndef FCW4_RING_NA
+#define FCW4_RING_NA 3
 #endif
 
 namespace fcs {
@@ -28,14 +32,21 @@ namespace {
 // straight-line stages that take the last HEAD positions of a period, then
 // runs the periods as a do-while: the padded schedule without its virtual
 // stages, no extra work, and still one control path.
-template <bool A_OC, bool B_OC, bool OUT_F32, int BN, int HEAD>
+//
+// NA = 2 mirrors the ring: two A tiles and three B tiles (ta2 is the third B
+// tile), A loads for stage t + 2 and B loads for stage t + 3, so the B
+// operand gets the longer lead.
+template <bool A_OC, bool B_OC, bool OUT_F32, int BN, int HEAD, int NA>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
     GemmArgs g) {
+    static_assert(NA == 3 || NA == 2, "three A and two B tiles, or two A and three B");
+    constexpr int NB = 5 - NA;
     constexpr int MF = 16, BKP = 64;
     constexpr int TN = BN / 32;        // 16-column blocks per wave
     constexpr int kT = 256 * BKP * 2;  // 32 KB per tile array (also one wave's epilogue staging)
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
     constexpr int kLB = DmaPP<B_OC, BKP, BN>::kInstr;
+    constexpr int kFar = NA == 3 ? kLA : kLB;  // loads of the operand with three tiles
     __shared__ __attribute__((aligned(1024))) char ta0[kT];
     __shared__ __attribute__((aligned(1024))) char ta1[kT];
     __shared__ __attribute__((aligned(1024))) char ta2[kT];
@@ -56,8 +67,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     bf16x8 fa[2][8], fb[2][TN];
 
-#define FCR_TA(I) ((I) == 0 ? ta0 : (I) == 1 ? ta1 : ta2)
-#define FCR_TB(I) ((I) == 0 ? tb0 : tb1)
+#define FCR_TA(I) (NA == 3 ? ((I) == 0 ? ta0 : (I) == 1 ? ta1 : ta2) : ((I) == 0 ? ta0 : ta1))
+#define FCR_TB(I) (NA == 3 ? ((I) == 0 ? tb0 : tb1) : ((I) == 0 ? tb0 : (I) == 1 ? tb1 : ta2))
 #define FCR_OFF(SIDX) (w.kbeg + (int64_t)((SIDX) < 0 ? 0 : (SIDX) < nkt ? (SIDX) : nkt - 1) * BKP)
 #define FCR_STEP_A(SIDX) (uint32_t)(A_OC ? FCR_OFF(SIDX) * g.lda * 2 : FCR_OFF(SIDX) * 2)
 #define FCR_STEP_B(SIDX) (uint32_t)(B_OC ? FCR_OFF(SIDX) * g.ldb * 2 : FCR_OFF(SIDX) * 2)
@@ -65,11 +76,12 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #define FCR_RB(SIDX) ((SIDX) < 0 ? rzb : w.rb)
     // 8 TN MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
     // set NXT; with LOADS, the B tile of stage T + 2 into LB, then the A tile
-    // of stage T + 3 into LA, placed as w64_read_after / w64_load_after say
+    // of stage T + 3 into LA (NA = 2: the A tile of T + 2, then the B tile of
+    // T + 3), placed as w64_read_after / w64_load_after say
 #define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, T)                                              \
     {                                                                                                  \
-        const uint32_t sb_ = FCR_STEP_B((T) + 2), sa_ = FCR_STEP_A((T) + 3);                           \
-        const __amdgpu_buffer_rsrc_t rb_ = FCR_RB((T) + 2), ra_ = FCR_RA((T) + 3);                     \
+        const uint32_t sb_ = FCR_STEP_B((T) + NB), sa_ = FCR_STEP_A((T) + NA);                         \
+        const __amdgpu_buffer_rsrc_t rb_ = FCR_RB((T) + NB), ra_ = FCR_RA((T) + NA);                   \
         constexpr int nl_ = (LOADS) ? kLA + kLB : 0;                                                   \
         _Pragma("unroll") for (int u = 0; u < 8 * TN; ++u) {                                           \
             mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], fa[CUR][u / TN]);                          \
@@ -80,22 +92,30 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + (r_ - 8) * MF, KS, lane);   \
             }                                                                                          \
             const int l_ = w64_load_after<TN>(nl_, u);                                                 \
-            if (l_ >= 0 && l_ < kLB)                                                                   \
-                db.issue_one(rb_, LB, sb_, wave, l_);                                                  \
-            else if (l_ >= kLB)                                                                        \
-                da.issue_one(ra_, LA, sa_, wave, l_ - kLB);                                            \
+            if constexpr (NA == 3) {                                                                   \
+                if (l_ >= 0 && l_ < kLB)                                                               \
+                    db.issue_one(rb_, LB, sb_, wave, l_);                                              \
+                else if (l_ >= kLB)                                                                    \
+                    da.issue_one(ra_, LA, sa_, wave, l_ - kLB);                                        \
+            } else {                                                                                   \
+                if (l_ >= 0 && l_ < kLA)                                                               \
+                    da.issue_one(ra_, LA, sa_, wave, l_);                                              \
+                else if (l_ >= kLA)                                                                    \
+                    db.issue_one(rb_, LB, sb_, wave, l_ - kLA);                                        \
+            }                                                                                          \
         }                                                                                              \
     }
-    // stage T with A tile P mod 3 and B tile P mod 2 (P = T mod 6): step 0,
-    // the barrier (only the A loads of the last step may still be in
-    // flight), step 1 (reads step 0 of stage T + 1)
+    // stage T with A tile P mod NA and B tile P mod NB (P = T mod 6): step 0,
+    // the barrier (only the loads of the operand with three tiles, issued
+    // last in the last step, may still be in flight), step 1 (reads step 0
+    // of stage T + 1)
 #define FCR_STAGE(P, T)                                                                                \
     {                                                                                                  \
-        FCR_STEP(0, 1, FCR_TA((P) % 3), FCR_TB((P) % 2), 1, false, ta0, tb0, T)                        \
-        waitcnt<kLA, 0>();                                                                             \
+        FCR_STEP(0, 1, FCR_TA((P) % NA), FCR_TB((P) % NB), 1, false, ta0, tb0, T)                      \
+        waitcnt<kFar, 0>();                                                                            \
         __builtin_amdgcn_s_barrier();                                                                  \
-        FCR_STEP(1, 0, FCR_TA(((P) + 1) % 3), FCR_TB(((P) + 1) % 2), 0, true, FCR_TA((P) % 3),         \
-                 FCR_TB((P) % 2), T)                                                                   \
+        FCR_STEP(1, 0, FCR_TA(((P) + 1) % NA), FCR_TB(((P) + 1) % NB), 0, true, FCR_TA((P) % NA),      \
+                 FCR_TB((P) % NB), T)                                                                  \
     }
 
     if (nkt > 0) {
@@ -106,13 +126,17 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             // -pad .. -1 go first and load through zero-size descriptors, so
             // their tiles hold zeros and their MFMAs add nothing.
             const int pad = (6 - nkt % 6) % 6;
-            // stages -pad, -pad + 1 and the A tile of -pad + 2; wait for the first; read its step 0
+            // stages -pad, -pad + 1 and the tile of -pad + 2 of the operand
+            // with three tiles; wait for the first; read its step 0
             da.issue_full(FCR_RA(-pad), ta0, FCR_STEP_A(-pad), wave);
             db.issue_full(FCR_RB(-pad), tb0, FCR_STEP_B(-pad), wave);
             da.issue_full(FCR_RA(1 - pad), ta1, FCR_STEP_A(1 - pad), wave);
             db.issue_full(FCR_RB(1 - pad), tb1, FCR_STEP_B(1 - pad), wave);
-            da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
-            waitcnt<2 * kLA + kLB, 0>();
+            if constexpr (NA == 3)
+                da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
+            else
+                db.issue_full(FCR_RB(2 - pad), ta2, FCR_STEP_B(2 - pad), wave);
+            waitcnt<kLA + kLB + kFar, 0>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
@@ -129,21 +153,25 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             }
         } else {
             // stages 0 .. HEAD - 1 take period positions P0 .. 5; stages 0, 1
-            // and the A tile of stage 2 go to those positions' tiles
+            // and stage 2's tile of the operand with three tiles go to those
+            // positions' tiles
             constexpr int P0 = 6 - HEAD;
-            da.issue_full(w.ra, FCR_TA(P0 % 3), FCR_STEP_A(0), wave);
-            db.issue_full(w.rb, FCR_TB(P0 % 2), FCR_STEP_B(0), wave);
-            da.issue_full(w.ra, FCR_TA((P0 + 1) % 3), FCR_STEP_A(1), wave);
-            db.issue_full(w.rb, FCR_TB((P0 + 1) % 2), FCR_STEP_B(1), wave);
-            da.issue_full(w.ra, FCR_TA((P0 + 2) % 3), FCR_STEP_A(2), wave);
-            waitcnt<2 * kLA + kLB, 0>();
+            da.issue_full(w.ra, FCR_TA(P0 % NA), FCR_STEP_A(0), wave);
+            db.issue_full(w.rb, FCR_TB(P0 % NB), FCR_STEP_B(0), wave);
+            da.issue_full(w.ra, FCR_TA((P0 + 1) % NA), FCR_STEP_A(1), wave);
+            db.issue_full(w.rb, FCR_TB((P0 + 1) % NB), FCR_STEP_B(1), wave);
+            if constexpr (NA == 3)
+                da.issue_full(w.ra, FCR_TA((P0 + 2) % 3), FCR_STEP_A(2), wave);
+            else
+                db.issue_full(w.rb, FCR_TB((P0 + 2) % 3), FCR_STEP_B(2), wave);
+            waitcnt<kLA + kLB + kFar, 0>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                fa[0][i] = fragment_mf<A_OC, BKP, MF>(FCR_TA(P0 % 3), wm0 + i * MF, 0, lane);
+                fa[0][i] = fragment_mf<A_OC, BKP, MF>(FCR_TA(P0 % NA), wm0 + i * MF, 0, lane);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(FCR_TB(P0 % 2), wn0 + j * MF, 0, lane);
+                fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(FCR_TB(P0 % NB), wn0 + j * MF, 0, lane);
             w4_acc_fence(acc);
             if constexpr (HEAD >= 5) FCR_STAGE(1, HEAD - 5)
             if constexpr (HEAD >= 4) FCR_STAGE(2, HEAD - 4)
@@ -188,35 +216,51 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         store_tile_bf16_staged(g, w.m0, w.n0, wm0, wn0, lane, acc, wave == 0 ? ta0 : wave == 1 ? ta1 : wave == 2 ? ta2 : tb0);
 }
 
+// Head forms that run out of registers and spill in their main loop are not
+// built; those cases run the padded form: at 256 columns, both operands
+// output-contiguous with three A tiles, and B output-contiguous with three B
+// tiles.
+constexpr bool head_spills(bool a_oc, bool b_oc) {
+    return FCW4_RING_BN == 256 && b_oc && (FCW4_RING_NA == 2 || a_oc);
+}
+#define FCW4_HEAD_SPILLS_RC_OC (FCW4_RING_BN == 256 && FCW4_RING_NA == 2)
+#define FCW4_HEAD_SPILLS_OC_OC (FCW4_RING_BN == 256)
+
 // Explicit instantiations (the host pass emits a launch stub for each): the
-// padded form and the head forms. With both operands output-contiguous at
-// 256 columns the head forms are not built (they spill); that case runs
-// the padded form.
-#define FCW4_RI(AOC, BOC, F32, HEAD) template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, FCW4_RING_BN, HEAD>(GemmArgs);
+// padded form and the head forms that are built.
+#define FCW4_RI(AOC, BOC, F32, HEAD) \
+    template __global__ void gemm_w4k64r_kernel<AOC, BOC, F32, FCW4_RING_BN, HEAD, FCW4_RING_NA>(GemmArgs);
 #define FCW4_RI3(AOC, BOC, F32) FCW4_RI(AOC, BOC, F32, -1) FCW4_RI(AOC, BOC, F32, 2) FCW4_RI(AOC, BOC, F32, 4)
+#define FCW4_RIH(AOC, BOC, F32) FCW4_RI(AOC, BOC, F32, 2) FCW4_RI(AOC, BOC, F32, 4)
 FCW4_RI3(false, false, false)
-FCW4_RI3(false, true, false)
-FCW4_RI3(true, false, false)
 FCW4_RI3(false, false, true)
-FCW4_RI3(false, true, true)
+FCW4_RI3(true, false, false)
 FCW4_RI3(true, false, true)
+FCW4_RI(false, true, false, -1)
+FCW4_RI(false, true, true, -1)
 FCW4_RI(true, true, false, -1)
 FCW4_RI(true, true, true, -1)
-#if FCW4_RING_BN != 256
-FCW4_RI(true, true, false, 2)
-FCW4_RI(true, true, false, 4)
-FCW4_RI(true, true, true, 2)
-FCW4_RI(true, true, true, 4)
+#if !FCW4_HEAD_SPILLS_RC_OC
+FCW4_RIH(false, true, false)
+FCW4_RIH(false, true, true)
 #endif
+#if !FCW4_HEAD_SPILLS_OC_OC
+FCW4_RIH(true, true, false)
+FCW4_RIH(true, true, true)
+#endif
+#undef FCW4_RIH
 #undef FCW4_RI3
 #undef FCW4_RI
+#undef FCW4_HEAD_SPILLS_RC_OC
+#undef FCW4_HEAD_SPILLS_OC_OC
 
 // the instance for a head form, or the padded one where no head form is
-// built; its name as profilers show it
+// built (the padded form is correct for any stage count); its name as
+// profilers show it
 template <bool AOC, bool BOC, bool F32, int HEAD>
 constexpr W4Kernel ring_entry(const char* name, const char* padded_name) {
-    constexpr bool padded = HEAD < 0 || (AOC && BOC && FCW4_RING_BN == 256);
-    return W4Kernel{gemm_w4k64r_kernel<AOC, BOC, F32, FCW4_RING_BN, padded ? -1 : HEAD>,
+    constexpr bool padded = HEAD < 0 || head_spills(AOC, BOC);
+    return W4Kernel{gemm_w4k64r_kernel<AOC, BOC, F32, FCW4_RING_BN, padded ? -1 : HEAD, FCW4_RING_NA>,
                     padded ? padded_name : name};
 }
 
@@ -224,12 +268,13 @@ constexpr W4Kernel ring_entry(const char* name, const char* padded_name) {
 
 #define FCW4_STR2(X) #X
 #define FCW4_STR(X) FCW4_STR2(X)
-#define FCW4_RN(AOC, BOC, F32, H) \
-    "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " FCW4_STR(FCW4_RING_BN) ", " #H ">"
+#define FCW4_RN(AOC, BOC, F32, H)                                                                                 \
+    "gemm_w4k64r_kernel<" #AOC ", " #BOC ", " #F32 ", " FCW4_STR(FCW4_RING_BN) ", " #H ", " FCW4_STR(FCW4_RING_NA) \
+    ">"
 #define FCW4_RE1(AOC, BOC, F32, H) ring_entry<AOC, BOC, F32, H>(FCW4_RN(AOC, BOC, F32, H), FCW4_RN(AOC, BOC, F32, -1))
 
 template <>
-W4Kernel w4_ring_kernel<FCW4_RING_BN>(int head, bool a_oc, bool b_oc, bool out_f32) {
+W4Kernel w4_ring_kernel<FCW4_RING_BN, FCW4_RING_NA>(int head, bool a_oc, bool b_oc, bool out_f32) {
 #define FCW4_RE(AOC, BOC, F32) \
     {FCW4_RE1(AOC, BOC, F32, -1), FCW4_RE1(AOC, BOC, F32, 2), FCW4_RE1(AOC, BOC, F32, 4)}
     // [out_f32][a_oc][b_oc][padded, head 2, head 4]
