@@ -19,8 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfcshard.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm_w4_ring256.hip", "gemm_w4_ring192.hip", "gemm_w4_ring256b.hip", "gemm_w4.hip", "gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip",
-           "fcshard_api.hip"]
+# largest first, so that the parallel build starts them first
+SOURCES = ["gemm_w4_ring256.hip", "gemm_w4_ring192.hip", "gemm_w4_ring256b.hip", "gemm_w4_ring192b.hip",
+           "gemm_w4.hip", "gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip"]
 
 # packed-fp32 instructions are switched off for all device code
 HIPCC_FLAGS = [

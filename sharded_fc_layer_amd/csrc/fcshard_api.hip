@@ -41,9 +41,9 @@ constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // 6-8: 4-wave, one wave per SIMD, 128 x 128 wave tiles (256 x 256), with
 // 32-value stages (6), 64-value stages in two LDS slots (7) or in a ring of
 // three A and two B tiles (8), or in the mirrored ring of two A and three B
-// tiles (9). Families 7 and 8 also run 256 x 192 block tiles (tile 2;
-// 128 x 96 per wave): where 256 x 256 tiles leave CUs idle (192 tiles on 256
-// CUs), 256 x 192 ones may fill them (256 tiles).
+// tiles (9). Families 7-9 also run 256 x 192 block tiles (tile 2; 128 x 96
+// per wave): where 256 x 256 tiles leave CUs idle (192 tiles on 256 CUs),
+// 256 x 192 ones may fill them (256 tiles).
 constexpr int kNumFamilies = 10;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
@@ -71,9 +71,7 @@ int encode_plan(int tile, int split_idx, int copy, int family) {
 }
 
 // block-tile width (output columns) of a one-wave-per-SIMD plan
-int w4_bn(const Plan& pl) {
-    return (pl.family == kFamilyW4 + 1 || pl.family == kFamilyW4 + 2) && pl.tile == 2 ? 192 : 256;
-}
+int w4_bn(const Plan& pl) { return pl.family > kFamilyW4 && pl.tile == 2 ? 192 : 256; }
 
 // One GEMM in kernel terms, resolved from an ABI call.
 struct Problem {

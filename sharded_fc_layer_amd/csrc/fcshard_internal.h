@@ -66,7 +66,7 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 // same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about
 // two stages to land; 3: the ring mirrored, with 2 A and 3 B tiles, so the B
 // operand's loads have the longer lead. bn is 256, or 192 for variants 1
-// and 2. The ring runs
+// to 3. The rings run
 // its reduction in periods of 6 stages; when every slice's stage count mod
 // 6 is 2 or 4 it starts with that many straight-line stages (the last
 // positions of a period), else it pads the front with zero stages.
@@ -84,9 +84,10 @@ struct W4Kernel {
 };
 
 // The ring kernel (variant 2 above) for block-tile width BN (256 or 192)
-// with NA A tiles and 5 - NA B tiles (3 + 2, or 2 + 3 for BN 256): head = 2
-// or 4 picks the head form, anything else the padded one. Defined in
-// gemm_w4_ring256.hip, gemm_w4_ring192.hip and gemm_w4_ring256b.hip.
+// with NA A tiles and 5 - NA B tiles (3 + 2, or 2 + 3): head = 2 or 4 picks
+// the head form, anything else the padded one. Defined in
+// gemm_w4_ring256.hip, gemm_w4_ring192.hip, gemm_w4_ring256b.hip and
+// gemm_w4_ring192b.hip.
 template <int BN, int NA>
 W4Kernel w4_ring_kernel(int head, bool a_oc, bool b_oc, bool out_f32);
 template <>
@@ -95,6 +96,8 @@ template <>
 W4Kernel w4_ring_kernel<192, 3>(int head, bool a_oc, bool b_oc, bool out_f32);
 template <>
 W4Kernel w4_ring_kernel<256, 2>(int head, bool a_oc, bool b_oc, bool out_f32);
+template <>
+W4Kernel w4_ring_kernel<192, 2>(int head, bool a_oc, bool b_oc, bool out_f32);
 
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

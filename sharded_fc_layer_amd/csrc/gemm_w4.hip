@@ -292,7 +292,9 @@ W4Kernel w4_entry(int variant, int bn, int head, bool a_oc, bool b_oc, bool out_
     if (variant == 2)
         return bn == 192 ? w4_ring_kernel<192, 3>(head, a_oc, b_oc, out_f32)
                          : w4_ring_kernel<256, 3>(head, a_oc, b_oc, out_f32);
-    if (variant == 3) return w4_ring_kernel<256, 2>(head, a_oc, b_oc, out_f32);
+    if (variant == 3)
+        return bn == 192 ? w4_ring_kernel<192, 2>(head, a_oc, b_oc, out_f32)
+                         : w4_ring_kernel<256, 2>(head, a_oc, b_oc, out_f32);
     const int row = variant == 0 ? 0 : bn == 192 ? 2 : 1;
     return kW4[row][(out_f32 ? 4 : 0) + (a_oc ? 2 : 0) + (b_oc ? 1 : 0)];
 }
@@ -307,7 +309,7 @@ const char* w4_kernel_name(int variant, int bn, bool a_oc, bool b_oc, bool out_f
 hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f32, const GemmArgs& args,
                           hipStream_t stream) {
     if (variant < 0 || variant > 3) return hipErrorInvalidValue;
-    if (bn != 256 && (variant == 0 || variant == 3 || bn != 192)) return hipErrorInvalidValue;
+    if (bn != 256 && (variant == 0 || bn != 192)) return hipErrorInvalidValue;
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + bn - 1) / bn) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
