@@ -2,9 +2,13 @@
 //  * transpose_bf16 - the "copy" arm of the layout tuner: rewrites an
 //    output-contiguous operand as reduction-contiguous, so the GEMM can run
 //    with both operands read along the reduction;
+//  * pad_rows_bf16  - copies a reduction-contiguous operand to rows padded
+//    with zeros to a whole number of 64-value stages;
 //  * splitk_reduce  - sums fp32 split-K partials in a fixed slice order and
 //    rounds once (bf16 nearest-even) or stores fp32;
 //  * fill_bf16      - deterministic values for the tuner's scratch operands.
+#include <algorithm>
+
 #include "fcshard_internal.h"
 
 namespace fcs {
@@ -112,6 +116,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// dst row r = src row r (cols values) then zeros up to ld; 8 values (16 B)
+// per thread and step, grid-stride over rows x ld / 8
+__global__ __launch_bounds__(256) void pad_rows_bf16_kernel(const uint16_t* __restrict__ src,
+                                                            uint16_t* __restrict__ dst, int64_t rows, int64_t cols,
+                                                            int64_t ld) {
+    const int64_t per_row = ld / 8, total = rows * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / per_row, c = (i - r * per_row) * 8;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (c < cols) v = *reinterpret_cast<const uint4*>(src + r * cols + c);
+        *reinterpret_cast<uint4*>(dst + r * ld + c) = v;
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, uint32_t seed) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -155,6 +173,17 @@ hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, bool a
                      ((uintptr_t)out % (out_f32 ? 16 : 8) == 0);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, out, out_f32,
                        out_f32 && accumulate, n, splits, stride, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, int64_t ld,
+                                hipStream_t stream) {
+    if (rows <= 0 || ld <= 0) return hipSuccess;
+    if (cols % 8 != 0 || ld % 8 != 0 || cols > ld || (uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0)
+        return hipErrorInvalidValue;
+    const int64_t work = rows * (ld / 8);
+    const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
+    hipLaunchKernelGGL(pad_rows_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, rows, cols, ld);
     return hipGetLastError();
 }
 

@@ -102,6 +102,13 @@ void split_geometry(int64_t K, int split, int64_t* k_split, int* slices) {
     *slices = (int)((K + ks - 1) / ks);
 }
 
+// Families 7-9 run reductions that are not a multiple of 64 by padding:
+// each reduction-contiguous operand is copied to rows of round_up(K, 64)
+// values with zeros past K (its last 64-value stage then reads zeros there),
+// while output-contiguous operands read zeros past row K through their
+// buffer bounds. Plans with a transpose copy do not pad.
+bool pads_reduction(const Problem& p, const Plan& pl) { return pl.family > kFamilyW4 && p.K % 64 != 0; }
+
 struct WsLayout {
     int64_t a_off, b_off, p_off, total;
 };
@@ -109,13 +116,15 @@ struct WsLayout {
 WsLayout ws_layout(const Problem& p, const Plan& pl) {
     WsLayout w{0, 0, 0, 0};
     int64_t off = 0;
-    if ((pl.copy & 1) && p.a_oc) {
+    const bool pad = pads_reduction(p, pl);
+    const int64_t kp = round_up(p.K, 64);
+    if (((pl.copy & 1) && p.a_oc) || (pad && !p.a_oc)) {
         w.a_off = off;
-        off += round_up(p.M * p.K * 2, 256);
+        off += round_up(p.M * (pad ? kp : p.K) * 2, 256);
     }
-    if ((pl.copy & 2) && p.b_oc) {
+    if (((pl.copy & 2) && p.b_oc) || (pad && !p.b_oc)) {
         w.b_off = off;
-        off += round_up(p.N * p.K * 2, 256);
+        off += round_up(p.N * (pad ? kp : p.K) * 2, 256);
     }
     int64_t ks;
     int slices;
@@ -138,16 +147,24 @@ bool plan_applies(const Problem& p, const Plan& pl) {
                                     ((pl.copy & 2) || (uintptr_t)p.B % 16 == 0);
     if (!aligned_after_copy && (pl.family != 1 || pl.tile != kUnalignedTile)) return false;
     if (pl.family >= 2 && pl.tile != 0 && !(w4_bn(pl) == 192)) return false;
-    if (pl.family >= kFamilyW4) {  // whole stages (pairs of 32- or 64-value stages for 6 and 7)
-        const int64_t q = pl.family == kFamilyW4 ? 64 : pl.family == kFamilyW4 + 1 ? 128 : 64;
+    if (pl.family >= kFamilyW4) {
         int64_t ks;
         int slices;
         split_geometry(p.K, pl.split, &ks, &slices);
-        if (p.K % q != 0 || (slices > 1 && ks % q != 0)) return false;
+        if (pl.family == kFamilyW4) {  // 32-value stages in pairs: whole 64-value units, no padding
+            if (p.K % 64 != 0 || ks % 64 != 0) return false;
+        } else if (pl.family == kFamilyW4 + 1) {  // 64-value stages in pairs: even stage counts
+            const int64_t first = (std::min(ks, p.K) + 63) / 64;
+            const int64_t last = (p.K - (int64_t)(slices - 1) * ks + 63) / 64;
+            if (first % 2 != 0 || last % 2 != 0) return false;
+        }
+        if (pads_reduction(p, pl) && pl.copy != 0) return false;
     }
     if (pl.family != 1) {
-        const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * p.K * 2);
-        const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * p.K * 2);
+        const int64_t k_a = pads_reduction(p, pl) && !p.a_oc ? round_up(p.K, 64) : p.K;
+        const int64_t k_b = pads_reduction(p, pl) && !p.b_oc ? round_up(p.K, 64) : p.K;
+        const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * k_a * 2);
+        const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * k_b * 2);
         if (a_bytes >= kPipeMaxBytes || b_bytes >= kPipeMaxBytes || p.M * p.K * 2 >= kPipeMaxBytes ||
             p.N * p.K * 2 >= kPipeMaxBytes)
             return false;
@@ -264,6 +281,21 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
         p.B = dst;
         p.b_oc = false;
         ldb = p.K;
+    }
+    if (pads_reduction(p0, pl)) {  // reduction-contiguous operands to rows of round_up(K, 64), zeros past K
+        const int64_t kp = round_up(p.K, 64);
+        if (!p.a_oc) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.a_off);
+            if ((e = launch_pad_rows_bf16(p.A, dst, p.M, p.K, kp, s)) != hipSuccess) return e;
+            p.A = dst;
+            lda = kp;
+        }
+        if (!p.b_oc) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.b_off);
+            if ((e = launch_pad_rows_bf16(p.B, dst, p.N, p.K, kp, s)) != hipSuccess) return e;
+            p.B = dst;
+            ldb = kp;
+        }
     }
     int64_t ks;
     int slices;

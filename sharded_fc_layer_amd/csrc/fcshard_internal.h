@@ -60,7 +60,11 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 
 // Enqueue the 4-wave (one wave per SIMD) GEMM, 256 x bn block tile, 128 x
 // bn / 2 per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
-// launch_gemm_pipe, and K a multiple of 64, of 128 for variant 1).
+// launch_gemm_pipe; variant 0: K and slices multiples of 64; variant 1: an
+// even number of 64-value stages per slice). A reduction that is not a
+// multiple of 64 ends with a partial stage: reduction-contiguous operands
+// must then have rows padded with zeros up to the next multiple of 64 (lda
+// / ldb the padded length); output-contiguous ones read zeros past row K.
 // variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
 // 2 slots (whole-cache-line rows for reduction-contiguous operands); 2: the
 // same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about
@@ -102,6 +106,11 @@ W4Kernel w4_ring_kernel<192, 2>(int head, bool a_oc, bool b_oc, bool out_f32);
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                  hipStream_t stream);
+
+// dst (rows x ld, row-major) = src (rows x cols, row-major) with zeros in
+// columns cols .. ld - 1; cols and ld multiples of 8, 16-byte aligned.
+hipError_t launch_pad_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, int64_t ld,
+                                hipStream_t stream);
 
 // out[i] = sum_{s < splits} ws[s * stride + i] (fixed order), stored bf16 or
 // fp32; with `accumulate` (fp32 only) out[i] = out[i] + that sum.
