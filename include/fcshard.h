@@ -130,8 +130,10 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
 
 /*
  * Describes the plan a hot call at this key would run: writes a NUL-terminated
- * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> ws=<bytes>"
- * into buf (truncated to len), followed by " tuned_ms=<t>" when fc_tune chose
+ * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> pad=<k>
+ * ws=<bytes>" into buf (truncated to len); pad is the length the reduction
+ * is zero-padded to (reduction-contiguous operands copied into the
+ * workspace), 0 for none. It is followed by " tuned_ms=<t>" when fc_tune chose
  * the plan (or a loaded plan file recorded its time): the median time of one
  * launch, in ms, as fc_tune measured it. Returns FC_E_INVALID for bad
  * arguments.

@@ -454,9 +454,9 @@ std::string describe(const Problem& p, int id) {
                                                             aligned);
     char buf[512];
     const char* tname = w4_bn(pl) == 192 ? "256x192" : kTiles[aligned ? pl.tile : kUnalignedTile].name;
-    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d ws=%lld", id, kname, tname, slices,
-                  pl.copy,
-                  (long long)ws_layout(p, pl).total);
+    const long long pad = pads_reduction(p, pl) ? (long long)round_up(p.K, 64) : 0;
+    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d pad=%lld ws=%lld", id, kname, tname,
+                  slices, pl.copy, pad, (long long)ws_layout(p, pl).total);
     return buf;
 }
 

@@ -170,7 +170,7 @@ def test_exact_integer_every_plan(shape):
                     assert st == F.FC_OK, F.status_str(st)
                     desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, dt)
                     assert desc["plan"] == pid
-                    what = f"{op} {shape} orders={xo}{wo} dtype={dt} plan={pid} {desc['kernel']}"
+                    what = f"{op} {shape} orders={xo}{wo} dtype={dt} plan={pid} {desc['kernel']} pad={desc['pad']}"
                     log(what)
                     G = host(c.gpu(op, dt))
                     torch.cuda.synchronize()
