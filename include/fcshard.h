@@ -37,11 +37,14 @@
  * synchronization, as for any asynchronous HIP call.
  *
  * Threading: the plan cache is guarded by a mutex; hot calls may come from
- * several host threads. Streams: plans with split-K or a transpose copy
- * (fc_plan_describe: split > 1 or copy != 0, i.e. ws > 0) stage data in the
- * device's one workspace, so two such calls that can run at the same time
- * on different streams race; order them (one stream, or events), or use
- * plans without workspace (fc_set_plan). Calls on one stream never race.
+ * several host threads. A workspace grows or is freed only while no other
+ * thread is enqueuing a hot call, and only after a device synchronization,
+ * so no enqueued kernel loses its workspace. Streams: plans with split-K, a
+ * transpose copy or a padded reduction (fc_plan_describe: ws > 0) stage data
+ * in the device's one workspace, and so does fc_tune while it times them;
+ * two such calls that can run at the same time on different streams race
+ * on its contents. Order them (one stream, or events), or use plans without
+ * workspace (fc_set_plan). Calls on one stream never race.
  * Determinism: the same plan on the same inputs gives bitwise-identical
  * output (split-K partials are summed in a fixed order, no atomics).
  */

@@ -203,7 +203,14 @@ struct PlanEntry {
     float ms;
 };
 
+// g_mu guards the plan cache and the device states. A hot call holds it from
+// reading the workspace pointer until its kernels are enqueued, so a growth
+// (which synchronizes the device before freeing) never frees a workspace that
+// an enqueued or about-to-be-enqueued kernel uses. g_ws_mu is held by every
+// call that may grow or free a workspace, or that runs the tuner's kernels on
+// it, for its whole duration; it is taken before g_mu.
 std::mutex g_mu;
+std::mutex g_ws_mu;
 std::map<Key, PlanEntry> g_plans;
 DevState g_dev[kMaxDevices];
 
@@ -398,25 +405,21 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
     if (st != FC_OK) return st;
     int dev;
     Plan pl;
-    void* ws = nullptr;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        if ((st = check_device(&dev)) != FC_OK) return st;
-        int id = -1;
-        auto it = g_plans.find(make_key(dev, op, M, K, N, xo, wo, dtype));
-        if (it != g_plans.end()) id = it->second.id;
-        if (id >= 0) {
-            pl = decode_plan(id);
-            // a plan that no longer applies (alignment) or lacks workspace falls back
-            if (!plan_applies(p, pl) || ws_layout(p, pl).total > g_dev[dev].ws_bytes) id = -1;
-        }
-        if (id < 0) pl = decode_plan(default_plan(p));
-        ws = g_dev[dev].ws;
+    std::lock_guard<std::mutex> lk(g_mu);  // held until the kernels are enqueued
+    if ((st = check_device(&dev)) != FC_OK) return st;
+    int id = -1;
+    auto it = g_plans.find(make_key(dev, op, M, K, N, xo, wo, dtype));
+    if (it != g_plans.end()) id = it->second.id;
+    if (id >= 0) {
+        pl = decode_plan(id);
+        // a plan that no longer applies (alignment) or lacks workspace falls back
+        if (!plan_applies(p, pl) || ws_layout(p, pl).total > g_dev[dev].ws_bytes) id = -1;
     }
+    if (id < 0) pl = decode_plan(default_plan(p));
     // the launchers report hipGetLastError(): drop an error that an earlier,
     // unrelated HIP call of this thread left behind
     (void)hipGetLastError();
-    return run_plan(p, pl, ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
+    return run_plan(p, pl, g_dev[dev].ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
 }
 
 fc_status grow_workspace(int dev, int64_t bytes) {
@@ -546,8 +549,9 @@ fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY, void* d
 
 int fc_plan_count(void) { return kNumPlans; }
 
-fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
-                      fc_out_dtype out_dtype, int plan_id) {
+// fc_set_plan with g_ws_mu already held by the caller
+static fc_status set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                          fc_out_dtype out_dtype, int plan_id) {
     if (bad_order(x_order) || bad_order(w_order) || bad_dtype(out_dtype)) return FC_E_INVALID;
     if (plan_id < -1 || plan_id >= kNumPlans) return FC_E_INVALID;
     int p_order = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : x_order;
@@ -571,6 +575,12 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
     if ((st = grow_workspace(dev, ws_layout(p, pl).total)) != FC_OK) return st;
     g_plans[key] = PlanEntry{plan_id, -1.0f};
     return FC_OK;
+}
+
+fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
+                      fc_out_dtype out_dtype, int plan_id) {
+    std::lock_guard<std::mutex> wl(g_ws_mu);
+    return set_plan(op, M, K, N, x_order, w_order, out_dtype, plan_id);
 }
 
 fc_status fc_plan_describe(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
@@ -608,6 +618,7 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
     if (bad_order(x_order) || bad_order(w_order) || bad_dtype(out_dtype)) return FC_E_INVALID;
     if (M < 1 || K < 1 || N < 1) return FC_E_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> wl(g_ws_mu);  // no growth or release while timing on the workspace
     int dev;
     {
         std::lock_guard<std::mutex> lk(g_mu);
@@ -751,6 +762,7 @@ fc_status fc_plans_save(const char* path) {
 
 fc_status fc_plans_load(const char* path) {
     if (!path) return FC_E_INVALID;
+    std::lock_guard<std::mutex> wl(g_ws_mu);
     int dev;
     {
         std::lock_guard<std::mutex> lk(g_mu);
@@ -774,7 +786,7 @@ fc_status fc_plans_load(const char* path) {
             break;
         }
         if (std::strcmp(arch, g_dev[dev].arch) != 0) continue;
-        fc_status st = fc_set_plan((fc_op)op, M, K, N, (fc_order)xo, (fc_order)wo, (fc_out_dtype)f32, id);
+        fc_status st = set_plan((fc_op)op, M, K, N, (fc_order)xo, (fc_order)wo, (fc_out_dtype)f32, id);
         if (st != FC_OK) {
             result = st;
             break;
@@ -801,6 +813,7 @@ const char* fc_status_str(fc_status status) {
 }
 
 fc_status fc_release(void) {
+    std::lock_guard<std::mutex> wl(g_ws_mu);
     std::lock_guard<std::mutex> lk(g_mu);
     g_plans.clear();
     fc_status st = FC_OK;
