@@ -28,7 +28,8 @@
  * output rows. No blocking, no reordering of the sum beyond that.
  *
  * Parity pins: tests/test_oracle_pins.py (exact rational brute force, closed
- * forms, invariants, a library fp64 product, the virtual-grid reassembly).
+ * forms, invariants, a library fp64 product, the virtual-grid reassembly) and
+ * tests/test_golden.py (a hand-computed worked example, tests/golden/).
  */
 #include <math.h>
 #include <stdint.h>
