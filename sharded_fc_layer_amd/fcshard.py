@@ -82,8 +82,9 @@ def _check(status: int, what: str) -> None:
 
 
 def _stream(stream) -> Optional[int]:
+    """A hipStream_t handle: from a torch.cuda.Stream, an int, or torch's current stream."""
     if stream is not None:
-        return int(stream)
+        return int(getattr(stream, "cuda_stream", stream))
     import torch
     return torch.cuda.current_stream().cuda_stream
 
@@ -112,7 +113,18 @@ def _out(out, rows: int, cols: int, out_dtype: int, like, name: str):
         return torch.empty((rows, cols), dtype=dt, device=like.device)
     if out.dtype != dt or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {(rows, cols)}")
+    if not out.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP tensor")
     return out
+
+
+def _one_device(*ts) -> None:
+    """The library runs on the current device: every tensor must live there."""
+    import torch
+    cur = torch.cuda.current_device()
+    for t in ts:
+        if t.device.index != cur:
+            raise ValueError(f"a tensor is on {t.device}, but the current device is cuda:{cur}")
 
 
 def fc_fwd(X, W, x_order: int = ROW, w_order: int = ROW, out=None, out_dtype: int = OUT_BF16, stream=None):
@@ -123,6 +135,7 @@ def fc_fwd(X, W, x_order: int = ROW, w_order: int = ROW, out=None, out_dtype: in
     if K2 != K:
         raise ValueError(f"inner dimensions differ: X is {M}x{K}, W is {K2}x{N}")
     Y = _out(out, M, N, out_dtype, X, "out")
+    _one_device(X, W, Y)
     _check(lib().fc_fwd(X.data_ptr(), x_order, W.data_ptr(), w_order, Y.data_ptr(), out_dtype, M, K, N,
                         _stream(stream)), "fc_fwd")
     return Y
@@ -136,6 +149,7 @@ def fc_bwd_data(dY, W, w_order: int = ROW, out=None, out_dtype: int = OUT_BF16, 
     if N2 != N:
         raise ValueError(f"dY is {M}x{N} but W is {K}x{N2}")
     dX = _out(out, M, K, out_dtype, dY, "out")
+    _one_device(dY, W, dX)
     _check(lib().fc_bwd_data(dY.data_ptr(), W.data_ptr(), w_order, dX.data_ptr(), out_dtype, M, K, N,
                              _stream(stream)), "fc_bwd_data")
     return dX
@@ -149,6 +163,7 @@ def fc_bwd_weight(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16
     if M2 != M:
         raise ValueError(f"X is {M}x{K} but dY is {M2}x{N}")
     dW = _out(out, K, N, out_dtype, X, "out")
+    _one_device(X, dY, dW)
     _check(lib().fc_bwd_weight(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
                                _stream(stream)), "fc_bwd_weight")
     return dW

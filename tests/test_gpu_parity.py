@@ -373,6 +373,21 @@ def test_overlapping_output_rejected_on_device():
     assert st == F.FC_E_INVALID
 
 
+def test_binding_rejects_host_output_and_takes_stream_objects():
+    X = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="CUDA/HIP"):
+        F.fc_fwd(X, W, out=torch.empty((64, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="CUDA/HIP"):
+        F.fc_bwd_weight(X, W, out=torch.empty((64, 64), dtype=torch.bfloat16))
+    X1, W1 = X + 1, W + 1
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the operands are written on the current stream
+    Y = F.fc_fwd(X1, W1, stream=s)
+    s.synchronize()
+    assert torch.equal(Y, torch.full((64, 64), 64.0, dtype=torch.bfloat16, device="cuda"))
+
+
 def test_runs_on_a_side_stream_and_tuned_equals_cold_plan_bits():
     M, K, N = 1024, 768, 1280
     d = I.make_random_inputs(M, K, N, seed=5)
