@@ -104,13 +104,21 @@ def _logical(t, order: int):
     return (r, c) if order == ROW else (c, r)
 
 
-def _out(out, rows: int, cols: int, out_dtype: int, like, name: str):
+def _out(out, rows: int, cols: int, out_dtype: int, like, name: str, stream=None):
+    """The output tensor: `out` checked, or a new one allocated on the stream that
+    writes it (so torch's caching allocator does not hand its memory to other
+    work on another stream while the kernels still write it)."""
     import torch
     dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
     if out is None:
         if out_dtype == OUT_F32_ACC:
             raise ValueError(f"{name}: accumulating needs the existing output tensor (out=)")
-        return torch.empty((rows, cols), dtype=dt, device=like.device)
+        if stream is None or _stream(stream) == torch.cuda.current_stream().cuda_stream:
+            return torch.empty((rows, cols), dtype=dt, device=like.device)
+        ts = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(_stream(stream), device=like.device)
+        with torch.cuda.stream(ts):
+            return torch.empty((rows, cols), dtype=dt, device=like.device)
     if out.dtype != dt or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {(rows, cols)}")
     if not out.is_cuda:
@@ -134,7 +142,7 @@ def fc_fwd(X, W, x_order: int = ROW, w_order: int = ROW, out=None, out_dtype: in
     K2, N = _logical(W, w_order)
     if K2 != K:
         raise ValueError(f"inner dimensions differ: X is {M}x{K}, W is {K2}x{N}")
-    Y = _out(out, M, N, out_dtype, X, "out")
+    Y = _out(out, M, N, out_dtype, X, "out", stream)
     _one_device(X, W, Y)
     _check(lib().fc_fwd(X.data_ptr(), x_order, W.data_ptr(), w_order, Y.data_ptr(), out_dtype, M, K, N,
                         _stream(stream)), "fc_fwd")
@@ -148,7 +156,7 @@ def fc_bwd_data(dY, W, w_order: int = ROW, out=None, out_dtype: int = OUT_BF16, 
     K, N2 = _logical(W, w_order)
     if N2 != N:
         raise ValueError(f"dY is {M}x{N} but W is {K}x{N2}")
-    dX = _out(out, M, K, out_dtype, dY, "out")
+    dX = _out(out, M, K, out_dtype, dY, "out", stream)
     _one_device(dY, W, dX)
     _check(lib().fc_bwd_data(dY.data_ptr(), W.data_ptr(), w_order, dX.data_ptr(), out_dtype, M, K, N,
                              _stream(stream)), "fc_bwd_data")
@@ -162,7 +170,7 @@ def fc_bwd_weight(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16
     M2, N = dY.shape
     if M2 != M:
         raise ValueError(f"X is {M}x{K} but dY is {M2}x{N}")
-    dW = _out(out, K, N, out_dtype, X, "out")
+    dW = _out(out, K, N, out_dtype, X, "out", stream)
     _one_device(X, dY, dW)
     _check(lib().fc_bwd_weight(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
                                _stream(stream)), "fc_bwd_weight")

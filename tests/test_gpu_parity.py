@@ -374,6 +374,7 @@ def test_overlapping_output_rejected_on_device():
 
 
 def test_binding_rejects_host_output_and_takes_stream_objects():
+    """Host outputs are refused; outputs it allocates for a side stream are allocated on that stream."""
     X = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     W = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError, match="CUDA/HIP"):
@@ -384,8 +385,10 @@ def test_binding_rejects_host_output_and_takes_stream_objects():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())  # the operands are written on the current stream
     Y = F.fc_fwd(X1, W1, stream=s)
+    Y2 = F.fc_fwd(X1, W1, stream=s.cuda_stream)  # a raw handle works the same
     s.synchronize()
-    assert torch.equal(Y, torch.full((64, 64), 64.0, dtype=torch.bfloat16, device="cuda"))
+    want = torch.full((64, 64), 64.0, dtype=torch.bfloat16, device="cuda")
+    assert torch.equal(Y, want) and torch.equal(Y2, want)
 
 
 def test_runs_on_a_side_stream_and_tuned_equals_cold_plan_bits():
