@@ -329,6 +329,20 @@ def _sample(n: int, k: int, rng) -> np.ndarray:
     return np.array(sorted(pick), dtype=np.int64)
 
 
+def _check_sampled(c, op, what, rng):
+    """Run op twice (bitwise equal), compare sampled outputs with the oracle."""
+    log(what)
+    Gt = c.gpu(op, F.OUT_BF16)
+    G2 = c.gpu(op, F.OUT_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(Gt.view(torch.int16), G2.view(torch.int16)), "not deterministic"
+    n_r, n_c = Gt.shape
+    rows, cols = _sample(n_r, 24, rng), _sample(n_c, 160, rng)
+    O, S = c.oracle(op, rows, cols)
+    G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    assert_close(G, O, S, F.OUT_BF16, what)
+
+
 FULL = [(2, 1, [(ROW, ROW)]), (2, 2, [(ROW, ROW)]), (2, 3, [(ROW, ROW)]), (2, 4, [(ROW, ROW)]),
         (3, 1, [(ROW, ROW)]), (4, 1, I.ORDER_PAIRS),
         (5, 1, [(ROW, ROW)]), (5, 2, [(ROW, ROW)]), (5, 3, [(ROW, ROW)]), (5, 4, [(ROW, ROW)]),
@@ -348,18 +362,20 @@ def test_full_size_sampled(workload, gemm, orders):
         F.fc_tune(g.M, g.K, g.N, xo, wo, F.OUT_BF16)
         for op in OPS:
             desc = F.fc_plan_describe(op_code(op), g.M, g.K, g.N, xo, wo, F.OUT_BF16)
-            what = f"w{workload}g{gemm} {op} orders={xo}{wo} {desc['kernel']} split={desc['split']} copy={desc['copy']}"
-            log(what)
-            Gt = c.gpu(op, F.OUT_BF16)
-            G2 = c.gpu(op, F.OUT_BF16)
-            torch.cuda.synchronize()
-            assert torch.equal(Gt.view(torch.int16), G2.view(torch.int16)), "not deterministic"
-            n_r, n_c = Gt.shape
-            rows, cols = _sample(n_r, 24, rng), _sample(n_c, 160, rng)
-            O, S = c.oracle(op, rows, cols)
-            G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
-            assert_close(G, O, S, F.OUT_BF16, what)
-            del Gt, G2
+            what = (f"w{workload}g{gemm} {op} orders={xo}{wo} {desc['kernel']} split={desc['split']} "
+                    f"copy={desc['copy']} pad={desc['pad']}")
+            _check_sampled(c, op, what, rng)
+        if g.N % 64:
+            # backward-data reduces over N, here not a multiple of 64: also force a
+            # plan that pads it, whatever the tuner picked
+            pid = next((p for p in range(F.fc_plan_count())
+                        if F.fc_set_plan(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16, p) == F.FC_OK
+                        and F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)["pad"] > 0),
+                       None)
+            assert pid is not None, "no padded plan applies"
+            desc = F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)
+            _check_sampled(c, "bwd_data", f"w{workload}g{gemm} bwd_data forced plan={pid} {desc['kernel']} "
+                                          f"pad={desc['pad']}", rng)
         del c
         torch.cuda.empty_cache()
 
