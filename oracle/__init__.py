@@ -156,15 +156,31 @@ def compare(G: np.ndarray, O: np.ndarray, S: np.ndarray, elem_tol: float = 1e-2,
             fro_tol: float = 5e-3) -> dict:
     """Tolerance check of a GPU result G (any float dtype) against (O, S).
 
-    Pass iff max |G - O| <= elem_tol * S elementwise and the relative Frobenius
-    error ||G - O|| / ||O|| <= fro_tol. A zero scale S demands an exact match.
+    The bound of the shard products: the elementwise error is at most
+    elem_tol times the magnitude scale S = |A|.|B| of that element, and the
+    relative Frobenius error ||G - O|| / ||O|| is at most fro_tol; both must
+    hold. A zero scale S demands an exact match of that element. When O is
+    zero everywhere the relative error is 0 for an exact match and infinite
+    otherwise. A NaN or an infinity in G is never within the bound.
     """
     G = np.asarray(G, dtype=np.float64)
+    O = np.asarray(O, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    if G.shape != O.shape or S.shape != O.shape:
+        raise ValueError(f"shapes differ: G {G.shape}, O {O.shape}, S {S.shape}")
+    finite = bool(np.all(np.isfinite(G)))
     err = np.abs(G - O)
     bound = elem_tol * S
-    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    with np.errstate(invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
     max_ratio = float(ratio.max()) if ratio.size else 0.0
     on = float(np.linalg.norm(O))
-    rel_fro = float(np.linalg.norm(G - O) / on) if on > 0 else float(np.linalg.norm(G - O))
+    diff = float(np.linalg.norm(G - O)) if finite else float("inf")
+    if on > 0:
+        rel_fro = diff / on
+    else:
+        rel_fro = 0.0 if diff == 0 else float("inf")
+    if not finite:
+        max_ratio = float("inf")
     return {"max_err_ratio": max_ratio, "rel_fro": rel_fro,
-            "pass": bool(max_ratio <= 1.0 and rel_fro <= fro_tol)}
+            "pass": bool(finite and max_ratio <= 1.0 and rel_fro <= fro_tol)}
