@@ -27,19 +27,27 @@
  *
  * Ownership. All data pointers are DEVICE pointers owned by the caller. The
  * library owns only its plan cache and one workspace per device, which grow
- * only inside fc_tune / fc_set_plan and are freed by fc_release.
+ * only inside fc_tune / fc_set_plan / fc_plans_load and are freed by
+ * fc_release.
  *
  * Hot calls (fc_fwd, fc_bwd_data, fc_bwd_weight) never allocate and never
  * synchronize: they validate, enqueue kernels on `stream` (a hipStream_t;
  * NULL is the null stream) and return. A shape that was never tuned runs a
- * default plan that needs no workspace. Errors are returned, never thrown;
- * the library never aborts. Device faults surface at the caller's next
- * synchronization, as for any asynchronous HIP call.
+ * default plan that needs no workspace; a hot call never launches a plan
+ * whose workspace is missing. Errors are returned, never thrown; the library
+ * never aborts. Device faults surface at the caller's next synchronization,
+ * as for any asynchronous HIP call.
+ *
+ * Graph capture. Hot calls may be captured into a HIP graph (they launch
+ * kernels only). A captured call that uses the workspace keeps its address:
+ * a later growth then retires that workspace instead of freeing it, so the
+ * graph stays valid until fc_release, which frees every workspace and so
+ * invalidates such graphs.
  *
  * Threading: the plan cache is guarded by a mutex; hot calls may come from
  * several host threads. A workspace grows or is freed only while no other
- * thread is enqueuing a hot call, and only after a device synchronization,
- * so no enqueued kernel loses its workspace. Streams: plans with split-K, a
+ * thread is enqueuing a hot call, and is freed only after a device
+ * synchronization, so no enqueued kernel loses its workspace. Streams: plans with split-K, a
  * transpose copy or a padded reduction (fc_plan_describe: ws > 0) stage data
  * in the device's one workspace, and so does fc_tune while it times them;
  * two such calls that can run at the same time on different streams race
@@ -160,6 +168,32 @@ fc_status fc_plans_save(const char* path);
  * malformed (entries before it stay loaded).
  */
 fc_status fc_plans_load(const char* path);
+
+/*
+ * Measurement aid, not part of the path: the empirical MFMA peak. The pages
+ * quote efficiency against an empirically measured peak
+ * (pith.science/paper/2502.08145, "Assumptions & free parameters"); this is
+ * the one of this chip for the GEMM kernels' instruction stream. One block of
+ * 4 waves per compute unit issues `iters` rounds of 64
+ * v_mfma_f32_16x16x32_bf16 per wave into 256 AGPR accumulators (the 128 x 128
+ * wave tile of the GEMMs), with no loads, LDS accesses or barriers. The
+ * result: the launch time (HIP events on `stream`), the bf16 flops issued,
+ * the compute-unit count, and the mean over blocks of the shader-clock
+ * counter's ticks per tick of the constant-rate counter (s_memtime over
+ * s_memrealtime; times wall_clock_mhz it is the engine clock in MHz when the
+ * first counter runs at the engine clock). Allocates and frees small
+ * buffers and synchronizes `stream`. FC_E_INVALID for a NULL result or iters
+ * outside 1 .. 2^40.
+ */
+typedef struct {
+    double ms;             /* kernel time */
+    double flops;          /* 2 x 16 x 16 x 32 per MFMA, every MFMA of the launch */
+    int compute_units;     /* blocks launched, one per compute unit */
+    double counter_ratio;  /* shader-clock counter ticks per constant-rate tick */
+    double wall_clock_mhz; /* rate of the constant-rate counter */
+} fc_mfma_probe_result;
+
+fc_status fc_mfma_probe(int64_t iters, fc_mfma_probe_result* out, void* stream);
 
 /* static text for a status; never NULL */
 const char* fc_status_str(fc_status status);

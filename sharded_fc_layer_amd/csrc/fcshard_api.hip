@@ -194,6 +194,12 @@ struct DevState {
     char arch[64] = {0};
     void* ws = nullptr;
     int64_t ws_bytes = 0;
+    // a hot call was captured into a graph while using the current workspace
+    bool ws_captured = false;
+    // workspaces superseded by a growth after such a capture: kept until
+    // fc_release, because captured kernels keep the workspace address they
+    // were captured with and may be replayed after the growth
+    std::vector<void*> retired;
 };
 
 // A cached plan and, when fc_tune chose it, its measured time (median of the
@@ -241,7 +247,7 @@ fc_status check_device(int* dev_out) {
 }
 
 // default plan: no workspace, no split; the largest tile that still gives
-// every CU work
+// every CU work (every plan it returns has ws_layout(...).total == 0)
 int default_plan(const Problem& p) {
     const int unaligned = encode_plan(kUnalignedTile, 0, 0, 1);
     if (!problem_aligned(p)) return unaligned;
@@ -258,8 +264,10 @@ int default_plan(const Problem& p) {
     // 64-value stages when the reduction allows it, else the 8-wave
     // ping-pong kernel; otherwise the 4-wave pipelined kernel with the
     // largest tile that still fills the chip
+    // (a reduction that is not a multiple of 64 would be padded through the
+    // workspace: not for a default plan)
     const int w64 = encode_plan(0, 0, 0, kFamilyW4 + 1);
-    if (tile == 0 && plan_applies(p, decode_plan(w64))) return w64;
+    if (tile == 0 && plan_applies(p, decode_plan(w64)) && ws_layout(p, decode_plan(w64)).total == 0) return w64;
     const int pp = encode_plan(0, 0, 0, 4);  // two-barrier ping-pong, 16x16x32
     if (tile == 0 && plan_applies(p, decode_plan(pp))) return pp;
     const int pipe = encode_plan(tile, 0, 0, 0);
@@ -416,19 +424,37 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
         if (!plan_applies(p, pl) || ws_layout(p, pl).total > g_dev[dev].ws_bytes) id = -1;
     }
     if (id < 0) pl = decode_plan(default_plan(p));
+    // never launch a plan whose workspace is not there
+    const int64_t ws_need = ws_layout(p, pl).total;
+    if (ws_need > g_dev[dev].ws_bytes) return FC_E_UNSUPPORTED;
+    if (ws_need > 0 && !g_dev[dev].ws_captured) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess &&
+            cs != hipStreamCaptureStatusNone)
+            g_dev[dev].ws_captured = true;
+    }
     // the launchers report hipGetLastError(): drop an error that an earlier,
     // unrelated HIP call of this thread left behind
     (void)hipGetLastError();
     return run_plan(p, pl, g_dev[dev].ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
 }
 
+// A larger workspace replaces the current one. The old one is freed after a
+// device synchronization (enqueued kernels may still use it), unless a hot
+// call was captured into a graph while using it: then it is retired and kept
+// until fc_release, so that replays of that graph stay valid.
 fc_status grow_workspace(int dev, int64_t bytes) {
     DevState& d = g_dev[dev];
     if (bytes <= d.ws_bytes) return FC_OK;
-    if (hipDeviceSynchronize() != hipSuccess) return FC_E_HIP;  // old workspace may be in use
-    if (d.ws) (void)hipFree(d.ws);
+    if (d.ws && d.ws_captured) {
+        d.retired.push_back(d.ws);
+    } else if (d.ws) {
+        if (hipDeviceSynchronize() != hipSuccess) return FC_E_HIP;
+        (void)hipFree(d.ws);
+    }
     d.ws = nullptr;
     d.ws_bytes = 0;
+    d.ws_captured = false;
     if (hipMalloc(&d.ws, (size_t)bytes) != hipSuccess) {
         d.ws = nullptr;
         (void)hipGetLastError();
@@ -818,13 +844,16 @@ fc_status fc_release(void) {
     g_plans.clear();
     fc_status st = FC_OK;
     for (int d = 0; d < kMaxDevices; ++d) {
-        if (g_dev[d].ws) {
+        if (g_dev[d].ws || !g_dev[d].retired.empty()) {
             int cur = 0;
             if (hipGetDevice(&cur) != hipSuccess) return FC_E_HIP;
             if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) st = FC_E_HIP;
-            (void)hipFree(g_dev[d].ws);
+            if (g_dev[d].ws) (void)hipFree(g_dev[d].ws);
+            for (void* r : g_dev[d].retired) (void)hipFree(r);
+            g_dev[d].retired.clear();
             g_dev[d].ws = nullptr;
             g_dev[d].ws_bytes = 0;
+            g_dev[d].ws_captured = false;
             (void)hipSetDevice(cur);
         }
     }
