@@ -41,11 +41,19 @@ OPS = {"fwd": F.OP_FWD, "bwd_data": F.OP_BWD_DATA, "bwd_weight": F.OP_BWD_WEIGHT
 
 
 class _Bufs:
-    def __init__(self, torch, M: int, K: int, N: int, copy_bytes: int):
-        g = torch.Generator(device="cuda").manual_seed(5)
-        self.X = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
-        self.W = (torch.randn((K, N), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-        self.dY = (torch.randn((M, N), device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    def __init__(self, torch, M: int, K: int, N: int, copy_bytes: int, host_inputs=None):
+        if host_inputs is not None:  # bf16 bit patterns (uint16), logical row-major
+            import numpy as np
+
+            def dev(bits):
+                return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+            self.X, self.W, self.dY = dev(host_inputs["X"]), dev(host_inputs["W"]), dev(host_inputs["dY"])
+        else:
+            g = torch.Generator(device="cuda").manual_seed(5)
+            self.X = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+            self.W = (torch.randn((K, N), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            self.dY = (torch.randn((M, N), device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
         self.Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         self.dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         self.dW = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
@@ -92,10 +100,13 @@ def cu_masked_stream(torch, cus: Sequence[int]):
 
 
 def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps: int = 7,
-            tune: bool = True, copy_cus: int = 0) -> List[Dict]:
+            tune: bool = True, copy_cus: int = 0, host_inputs=None, return_output: bool = False) -> List[Dict]:
     """One record per message size (see the module docstring). With copy_cus > 0
     the copy's stream runs on that many compute units, spread over the chip,
-    and the GEMM's stream on the others (CU-masked streams)."""
+    and the GEMM's stream on the others (CU-masked streams). host_inputs: the
+    operands as bf16 bit patterns ({"X", "W", "dY"}, logical row-major; default
+    torch.randn on the device). return_output: each record also holds, under
+    "output", the GEMM's output written while the copy ran, as a host tensor."""
     import torch
     if op not in OPS:
         raise ValueError(f"op must be one of {sorted(OPS)}")
@@ -113,7 +124,7 @@ def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps:
     full = torch.cuda.current_stream()
     out = []
     for mb in copy_mbytes:
-        b = _Bufs(torch, M, K, N, int(mb * 1e6))
+        b = _Bufs(torch, M, K, N, int(mb * 1e6), host_inputs)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
 
         def flush():
@@ -167,6 +178,8 @@ def measure(M: int, K: int, N: int, op: str, copy_mbytes: Sequence[float], reps:
                     "gemm_all_cus_ms": round(statistics.median(x[0] for x in whole), 4) if whole else None,
                     "gemm_slowdown": round(t_g_under / t_g, 4),
                     "hidden_fraction": round((t_g + t_c - t_both) / t_c, 4), "output_identical": same})
+        if return_output:
+            out[-1]["output"] = res.cpu()
         del b
         torch.cuda.empty_cache()
     return out

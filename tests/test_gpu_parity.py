@@ -180,6 +180,39 @@ def test_exact_integer_every_plan(shape):
                 F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, -1)
 
 
+def test_default_plans_need_no_workspace():
+    """Untuned shapes run a plan that needs no workspace, also where the
+    one-wave-per-SIMD kernels could only run the reduction padded (K = 2040 is
+    not a multiple of 64), and right after fc_release (no workspace at all).
+    Exact on whole sampled rows and columns of integer-valued data."""
+    M, K, N = 4096, 2040, 4096
+    F.fc_release()
+    for xo, wo in ALL_ORDERS:
+        for op in OPS:
+            for dt in (F.OUT_BF16, F.OUT_F32):
+                desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, dt)
+                # (a plan whose operands are both output-contiguous pads the
+                # reduction with no workspace: rows past K read zeros)
+                assert desc["ws"] == 0, f"{op} orders={xo}{wo} dtype={dt}: {desc}"
+    d = I.make_integer_inputs(M, K, N, seed=13)
+    rng = np.random.default_rng(13)
+    for xo, wo in ((ROW, ROW), (COL, ROW)):
+        c = Case(d, xo, wo)
+        for op in OPS:
+            desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, F.OUT_BF16)
+            what = f"default plan {op} orders={xo}{wo} {desc['kernel']} pad={desc['pad']}"
+            log(what)
+            Gt = c.gpu(op, F.OUT_BF16)
+            torch.cuda.synchronize()
+            n_r, n_c = Gt.shape
+            rows, cols = _sample(n_r, 6, rng), _sample(n_c, 6, rng)
+            O, _ = c.oracle(op, rows, None)
+            assert_exact(host(Gt[torch.from_numpy(rows).cuda()]), O, F.OUT_BF16, what + " rows")
+            O, _ = c.oracle(op, None, cols)
+            assert_exact(host(Gt[:, torch.from_numpy(cols).cuda()].contiguous()), O, F.OUT_BF16, what + " cols")
+        del c
+
+
 # ------------------------------------------------ accumulating fp32 output
 
 def _out_shape(op, M, K, N):
@@ -337,10 +370,13 @@ def _check_sampled(c, op, what, rng):
     torch.cuda.synchronize()
     assert torch.equal(Gt.view(torch.int16), G2.view(torch.int16)), "not deterministic"
     n_r, n_c = Gt.shape
-    rows, cols = _sample(n_r, 24, rng), _sample(n_c, 160, rng)
-    O, S = c.oracle(op, rows, cols)
-    G = host(Gt[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
-    assert_close(G, O, S, F.OUT_BF16, what)
+    # whole sampled rows and whole sampled columns: every tile row and every
+    # tile column of the output is touched
+    rows, cols = _sample(n_r, 8, rng), _sample(n_c, 8, rng)
+    O, S = c.oracle(op, rows, None)
+    assert_close(host(Gt[torch.from_numpy(rows).cuda()]), O, S, F.OUT_BF16, what + " rows")
+    O, S = c.oracle(op, None, cols)
+    assert_close(host(Gt[:, torch.from_numpy(cols).cuda()].contiguous()), O, S, F.OUT_BF16, what + " cols")
 
 
 FULL = [(2, 1, [(ROW, ROW)]), (2, 2, [(ROW, ROW)]), (2, 3, [(ROW, ROW)]), (2, 4, [(ROW, ROW)]),

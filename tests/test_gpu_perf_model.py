@@ -52,7 +52,26 @@ def test_measure_rank_validate(tmp_path):
     assert not missing and len(done) == len(PM.grids(4))
     r = PM.validate(model, PM.Grid(1, 2, 1, 2), p, steps=10, warmup=3)
     log(str(r))
-    assert r["gemms"] == 12 and 0.3 < r["predicted_over_measured"] < 3.0
+    # this model's shards are launch-bound (a few microseconds each): the
+    # plumbing is checked here, the accuracy on shards of a real size below
+    assert r["gemms"] == 12 and r["predicted_ms"] > 0 and r["measured_ms"] > 0
+    F.fc_release()
+
+
+def test_compute_term_accuracy(tmp_path):
+    """Hidden 2048, FFN 8192, 16384 tokens on the 1x2x1x2 grid (shards of 8192
+    tokens; 0.07-0.2 ms per product): the sum of the tuned single-launch times
+    predicts the back-to-back stream within 15 %."""
+    model = PM.Model("gpt_h2048", 2048, 8192, 1, 0, 16384)
+    grid = PM.Grid(1, 2, 1, 2)
+    p = str(tmp_path / "plans.txt")
+    F.fc_release()
+    for s in PM.shards(model, grid):
+        F.fc_tune(s.M, s.K, s.N)
+    F.fc_plans_save(p)
+    r = PM.validate(model, grid, p, steps=20, warmup=5)
+    log(str(r))
+    assert r["gemms"] == 12 and 0.85 < r["predicted_over_measured"] < 1.15
     F.fc_release()
 
 
