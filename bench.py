@@ -2,21 +2,30 @@
 """Throughput of one GPU's FC-layer shard GEMMs (forward + both backward
 products) on an MI355X, through the library's C ABI.
 
-A step is one pass of the hot path over one batch of synthetic inputs: for
+A step is one pass of the hot path over one batch of synthetic input: for
 every FC layer of the workload, forward Y = X.W, backward-data dX = dY.W^T
 and backward-weight dW = X^T.dY, issued back to back on one HIP stream
-(bf16 in, fp32 accumulate, bf16 out), with the plans fc_tune picked (tuning
-runs before the timed region). Inputs are resident in HBM before timing.
+(bf16 in, fp32 accumulate, bf16 out) in training-step order (the forwards
+layer by layer, then the backward products in reverse), with the plans
+fc_tune picked (tuning runs before the timed region). Inputs are seeded
+synthetic bf16 (N(0, 1) activations, N(0, 0.02) weights, N(0, 1e-3) output
+gradients), resident in HBM before timing.
 
-Default workload: the GPT-style block with hidden 2048 and 8192 tokens
-(QKV 2048->6144, attention-out 2048->2048, MLP up 2048->8192, MLP down
-8192->2048), i.e. 12 GEMMs per step.
+Default workload: one GPU's shard of a 405B-like layer (hidden 16384, FFN
+53248, 128 heads) on a virtual 2 x 4 x 2 grid with 8192 tokens per shard,
+plus a 16384 x 16032 vocabulary-projection shard: QKV 8192 -> 12288,
+out-projection 8192 -> 4096, MLP up 8192 -> 13312, MLP down 26624 -> 4096,
+vocabulary 16384 -> 16032, i.e. 15 GEMMs per step.
 
 Prints ONE JSON line. `value` is TFLOP/s (2 M K N per GEMM, summed over the
-step, divided by the mean step time). `roofline` reports the dominant kernel
-(largest summed time) against the dense bf16 MFMA peak, from HIP events
-recorded on the launch stream around each of its launches. `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+step, divided by the mean step time); the mean of the last 8 steps, the
+median, min and max are given beside it. `roofline` reports the dominant
+kernel (largest summed time) against the dense bf16 MFMA peak, from HIP
+events recorded on the launch stream around each of its launches.
+`clock` gives the engine clock sampled during a second pass of the step, the
+empirical per-CU MFMA rate of the MFMA-only probe kernel, and the step's
+fraction of the clock-scaled peak. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -83,7 +92,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    p.add_argument("--workload", type=int, default=5, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--no-extra", action="store_true", help="skip the large-shard context workloads")
     p.add_argument("--no-tune", action="store_true", help="use the default plans")
@@ -93,6 +102,9 @@ def parse():
                    help="CPU oracle timing: the sample doubles until one pass takes at least half of this")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device copy (a known-size reference for HBM counters)")
+    p.add_argument("--no-clock", action="store_true", help="skip the clock pass and the MFMA-only probe")
+    p.add_argument("--probe-iters", type=int, default=60000,
+                   help="MFMA-only probe: rounds of 64 MFMAs per wave (60000: about 0.5 s)")
     return p.parse_args()
 
 
@@ -128,15 +140,17 @@ class Layer:
 
 
 def make_layers(workload, torch, F, I, host_inputs, xo=0, wo=0):
+    """Device buffers of every FC shard of a workload: the seeded host inputs
+    (host_inputs=True; X and W stored in orders xo, wo), or draws of the same
+    distributions on the device."""
     import numpy as np
-    if host_inputs and (xo or wo):
-        raise ValueError("host inputs are generated row-major only")
     layers = []
     for gi, g in enumerate(I.WORKLOADS[workload], start=1):
         if host_inputs:
             d = I.make_inputs(workload, gi)
-            dev = lambda b: torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16)  # noqa: E731
-            layers.append(Layer(g, dev(d["X"]), dev(d["W"]), dev(d["dY"]), torch, F))
+            dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to("cuda").view(torch.bfloat16)  # noqa: E731
+            layers.append(Layer(g, dev(I.stored(d["X"], xo)), dev(I.stored(d["W"], wo)), dev(d["dY"]), torch, F,
+                                xo, wo))
             del d
         else:
             gen = torch.Generator(device="cuda").manual_seed(1000 * workload + gi)
@@ -145,6 +159,108 @@ def make_layers(workload, torch, F, I, host_inputs, xo=0, wo=0):
             W = rn(g.K, g.N, g.sw) if wo == 0 else rn(g.N, g.K, g.sw)
             layers.append(Layer(g, X, W, rn(g.M, g.N, g.sdy), torch, F, xo, wo))
     return layers
+
+
+class ClockSampler:
+    """Samples the engine (gfx) clock and the socket power of the device in a
+    background thread, through amdsmi (read-only metrics; no GPU work)."""
+
+    def __init__(self, torch, interval_s=0.005):
+        import amdsmi
+        self.smi, self.interval = amdsmi, interval_s
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            raise RuntimeError("amdsmi sees no GPU")
+        self.h = handles[0]
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        if bus is not None and len(handles) > 1:
+            for h in handles:  # the handle whose PCI bus is torch's device 0
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == int(bus):
+                    self.h = h
+                    break
+        self.samples, self._stop, self._thread = [], False, None
+
+    def read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        pw = m.get("current_socket_power")
+        return (float(clk) if isinstance(clk, (int, float)) else None,
+                float(pw) if isinstance(pw, (int, float)) and 0 < pw < 10000 else None)
+
+    def _run(self):
+        import threading  # noqa: F401
+        while not self._stop:
+            try:
+                self.samples.append((time.perf_counter(),) + self.read())
+            except Exception:  # a failed read leaves a gap, not an error
+                pass
+            time.sleep(self.interval)
+
+    def start(self):
+        import threading
+        self.samples, self._stop = [], False
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._stop = True
+        self._thread.join()
+        clk = [c for _, c, _ in self.samples if c]
+        pw = [p for _, _, p in self.samples if p]
+        return {"samples": len(self.samples), "clock_mhz_mean": sum(clk) / len(clk) if clk else None,
+                "clock_mhz_min": min(clk) if clk else None, "clock_mhz_max": max(clk) if clk else None,
+                "socket_power_w_mean": sum(pw) / len(pw) if pw else None}
+
+    def close(self):
+        try:
+            self.smi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def clock_and_probe(layers, steps, args, torch, F):
+    """The engine clock during a second pass of the step, the MFMA-only probe
+    (the GEMM kernels' MFMA stream alone: the empirical per-CU bf16 rate and
+    the clock it holds), and the step's fraction of the clock-scaled peak:
+    compute units x the probe's flop per clock per CU x the step's clock."""
+    res = {"source": "amdsmi gpu_metrics current_gfxclks, sampled every 5 ms"}
+    try:
+        smp = ClockSampler(torch)
+    except Exception as e:  # no metrics: report the probe alone
+        smp = None
+        res["source"] = f"unavailable ({type(e).__name__}: {e})"
+    flops = step_flops(layers)
+    if smp:
+        smp.start()
+    ms, _, _ = run_timed(layers, steps, 3, torch)
+    step_clock = smp.stop() if smp else None
+    res["step_pass"] = {"steps": steps, "ms_per_step": round(ms, 4),
+                        "tflops": round(flops / (ms / 1e3) / 1e12, 2), "clock": step_clock}
+    if smp:
+        smp.start()
+    pr = F.fc_mfma_probe(args.probe_iters)
+    probe_clock = smp.stop() if smp else None
+    if smp:
+        smp.close()
+    rate = pr["flops"] / (pr["ms"] / 1e3)
+    res["mfma_probe"] = {"ms": round(pr["ms"], 3), "tflops": round(rate / 1e12, 2),
+                         "compute_units": pr["compute_units"], "clock": probe_clock,
+                         "counter_ratio": round(pr["counter_ratio"], 4), "wall_clock_mhz": pr["wall_clock_mhz"],
+                         "kernel": "mfma_probe_kernel: 64 v_mfma_f32_16x16x32_bf16 per round, 256 AGPR "
+                                   "accumulators per wave, one wave per SIMD, no loads / LDS / barriers"}
+    pc = probe_clock and probe_clock["clock_mhz_mean"]
+    sc = step_clock and step_clock["clock_mhz_mean"]
+    if pc and sc:
+        per_cu = rate / (pr["compute_units"] * pc * 1e6)  # bf16 flop per clock per CU
+        peak = pr["compute_units"] * per_cu * sc * 1e6 / 1e12
+        res.update({"clock_GHz": round(sc / 1e3, 4), "probe_clock_GHz": round(pc / 1e3, 4),
+                    "flop_per_clock_per_cu": round(per_cu, 1),
+                    "clock_scaled_peak": round(peak, 1),
+                    "frac_clock": round(res["step_pass"]["tflops"] / peak, 4)})
+    return res
 
 
 def step_calls(layers):
@@ -220,7 +336,7 @@ def plans_of(layers, F, kern=None):
         for opname, op, _ in L.calls():
             d = F.fc_plan_describe(op, g.M, g.K, g.N)
             rec = {"gemm": g.name, "op": opname, "M": g.M, "K": g.K, "N": g.N, "kernel": d["kernel"],
-                   "split": d["split"], "copy": d["copy"]}
+                   "split": d["split"], "copy": d["copy"], "pad": d["pad"]}
             ms = by_call.get((g.name, opname))
             if ms:
                 avg = sum(ms) / len(ms)
@@ -384,28 +500,40 @@ def main():
         "device": props.name,
     }
 
+    if not args.no_clock:
+        result["clock"] = clock_and_probe(layers, args.steps, args, torch, F)
+        c = result["clock"]
+        log(f"clock pass: {c['step_pass']}; probe {c['mfma_probe']['tflops']} TFLOP/s; "
+            f"frac_clock {c.get('frac_clock')}")
+        for k in ("clock_GHz", "clock_scaled_peak", "frac_clock"):
+            result[k] = c.get(k)
+
     if not args.no_extra:
-        extra = {}
         del layers
         torch.cuda.empty_cache()
-        for w in (3, 5):
-            Ls = make_layers(w, torch, F, I, host_inputs=False)
+        context = {}
+        for w in (2, 3, 5):  # every other workload of one or more FC shards, row-major
+            if w == args.workload:
+                continue
+            Ls = make_layers(w, torch, F, I, host_inputs=True)
             if not args.no_tune:
                 for L in Ls:
                     F.fc_tune(L.g.M, L.g.K, L.g.N)
             wms, wsteps, _ = run_timed(Ls, 10, 3, torch)
             wf = step_flops(Ls)
-            extra[WORKLOAD_NAMES[w]] = {"tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
-                                        "pct_of_mfma_peak": round(100 * wf / (wms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
-                                        "gemms_per_step": 3 * len(Ls)}
-            log(f"workload {w}: {extra[WORKLOAD_NAMES[w]]}")
+            context[WORKLOAD_NAMES[w]] = {
+                "tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
+                "mean_last8_ms": round(float(np.mean(wsteps[-8:])), 3),
+                "pct_of_mfma_peak": round(100 * wf / (wms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1),
+                "gemms_per_step": 3 * len(Ls)}
+            log(f"workload {w}: {context[WORKLOAD_NAMES[w]]}")
             del Ls
             torch.cuda.empty_cache()
-        result["large_shard_context"] = extra
+        result["workload_context"] = context
         # the layout sweep: the skinny shard in each storage-order pair
         sweep = {}
         for xo, wo in I.ORDER_PAIRS:
-            Ls = make_layers(4, torch, F, I, host_inputs=False, xo=xo, wo=wo)
+            Ls = make_layers(4, torch, F, I, host_inputs=True, xo=xo, wo=wo)
             if not args.no_tune:
                 for L in Ls:
                     F.fc_tune(L.g.M, L.g.K, L.g.N, xo, wo)
@@ -419,9 +547,9 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         result["layout_sweep_context"] = {"workload": WORKLOAD_NAMES[4], "gemms_per_step": 3, "by_orders": sweep}
-        # the same step with every dW added into an fp32 gradient buffer
+        # the GPT-block step with every dW added into an fp32 gradient buffer
         # (accumulation over micro-batches), for context
-        Ls = make_layers(args.workload, torch, F, I, host_inputs=False)
+        Ls = make_layers(2, torch, F, I, host_inputs=True)
         for L in Ls:
             L.dW32 = torch.zeros((L.g.K, L.g.N), dtype=torch.float32, device="cuda")
             if not args.no_tune:
@@ -430,6 +558,7 @@ def main():
         wms, _, _ = run_timed(Ls, 10, 3, torch)
         wf = step_flops(Ls)
         result["dw_accumulate_context"] = {
+            "workload": WORKLOAD_NAMES[2],
             "tflops": round(wf / (wms / 1e3) / 1e12, 1), "ms_per_step": round(wms, 3),
             "dw_dtype": "fp32, added into (FC_OUT_F32_ACCUMULATE)",
             "dw_extra_bytes_per_step": int(sum(6 * L.g.K * L.g.N for L in Ls))}

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 # largest first, so that the parallel build starts them first
 SOURCES = ["gemm_w4_ring256.hip", "gemm_w4_ring192.hip", "gemm_w4_ring256b.hip", "gemm_w4_ring192b.hip",
-           "gemm_w4.hip", "gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "fcshard_api.hip"]
+           "gemm_w4.hip", "gemm_pipe.hip", "gemm_bf16.hip", "aux_kernels.hip", "mfma_probe.hip", "fcshard_api.hip"]
 
 # packed-fp32 instructions are switched off for all device code
 HIPCC_FLAGS = [

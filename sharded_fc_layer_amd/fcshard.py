@@ -28,6 +28,12 @@ FC_OK, FC_E_INVALID, FC_E_UNSUPPORTED, FC_E_HIP, FC_E_NOMEM = 0, 1, 2, 3, 4
 _lib = None
 
 
+class MfmaProbeResult(ctypes.Structure):
+    """fc_mfma_probe_result of include/fcshard.h."""
+    _fields_ = [("ms", ctypes.c_double), ("flops", ctypes.c_double), ("compute_units", ctypes.c_int),
+                ("counter_ratio", ctypes.c_double), ("wall_clock_mhz", ctypes.c_double)]
+
+
 class FcError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_str(status)}")
@@ -65,8 +71,9 @@ def lib() -> ctypes.CDLL:
         L.fc_release.argtypes = []
         L.fc_plans_save.argtypes = [ctypes.c_char_p]
         L.fc_plans_load.argtypes = [ctypes.c_char_p]
+        L.fc_mfma_probe.argtypes = [i64, ctypes.POINTER(MfmaProbeResult), vp]
         for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
-                  L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load):
+                  L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load, L.fc_mfma_probe):
             f.restype = ci
         _lib = L
     return _lib
@@ -220,3 +227,12 @@ def fc_plans_load(path: str) -> None:
 
 def fc_release() -> None:
     _check(lib().fc_release(), "fc_release")
+
+
+def fc_mfma_probe(iters: int = 100000, stream=None) -> dict:
+    """The MFMA-only stream of the GEMM kernels on every compute unit (measurement
+    aid): launch time, flops, compute units and the shader-clock counter ratio."""
+    r = MfmaProbeResult()
+    _check(lib().fc_mfma_probe(int(iters), ctypes.byref(r), _stream(stream)), "fc_mfma_probe")
+    return {"ms": r.ms, "flops": r.flops, "compute_units": r.compute_units, "counter_ratio": r.counter_ratio,
+            "wall_clock_mhz": r.wall_clock_mhz}
