@@ -222,44 +222,65 @@ class ClockSampler:
 
 
 def clock_and_probe(layers, steps, args, torch, F):
-    """The engine clock during a second pass of the step, the MFMA-only probe
-    (the GEMM kernels' MFMA stream alone: the empirical per-CU bf16 rate and
-    the clock it holds), and the step's fraction of the clock-scaled peak:
-    compute units x the probe's flop per clock per CU x the step's clock."""
-    res = {"source": "amdsmi gpu_metrics current_gfxclks, sampled every 5 ms"}
+    """The engine clock during the step, the MFMA-only probe (the GEMM kernels'
+    MFMA stream alone: the empirical bf16 flop per clock per CU), and the
+    step's fraction of the clock-scaled peak: compute units x that rate x the
+    step's clock.
+
+    The clock is read on the GPU itself: in a second pass of the step, a
+    short launch of the probe kernel (16 rounds of 64 MFMAs per wave, a few
+    microseconds) follows every GEMM, and each of its blocks reads the
+    shader-clock counter against the constant-rate counter; the chip's clock
+    moves on a millisecond scale, so that is the clock the GEMM ran at. The
+    step's clock is the mean over GEMMs weighted by their flops. Socket power
+    is sampled through amdsmi meanwhile."""
+    import numpy as np
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pr = F.fc_mfma_probe(args.probe_iters)
+    wall_mhz = pr["wall_clock_mhz"]
+    probe_ghz = pr["counter_ratio"] * wall_mhz / 1e3
+    rate = pr["flops"] / (pr["ms"] / 1e3)
+    per_cu = rate / (pr["compute_units"] * probe_ghz * 1e9)  # bf16 flop per clock per CU
+    res = {"mfma_probe": {"ms": round(pr["ms"], 3), "tflops": round(rate / 1e12, 2),
+                          "compute_units": pr["compute_units"], "clock_GHz": round(probe_ghz, 4),
+                          "flop_per_clock_per_cu": round(per_cu, 1),
+                          "frac_of_4096_per_clock": round(per_cu / 4096, 4),
+                          "kernel": "mfma_probe_kernel: 64 v_mfma_f32_16x16x32_bf16 per round, 256 AGPR "
+                                    "accumulators per wave, one wave per SIMD, no loads / LDS / barriers"}}
+    calls = step_calls(layers)
+    clocks = torch.zeros((steps * len(calls), cus, 4), dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        for _, (_, _, fn) in calls:
+            fn()
+    torch.cuda.synchronize()
     try:
         smp = ClockSampler(torch)
-    except Exception as e:  # no metrics: report the probe alone
-        smp = None
-        res["source"] = f"unavailable ({type(e).__name__}: {e})"
-    flops = step_flops(layers)
-    if smp:
         smp.start()
-    ms, _, _ = run_timed(layers, steps, 3, torch)
-    step_clock = smp.stop() if smp else None
-    res["step_pass"] = {"steps": steps, "ms_per_step": round(ms, 4),
-                        "tflops": round(flops / (ms / 1e3) / 1e12, 2), "clock": step_clock}
+    except Exception as e:  # no power readings: the clock comes from the GPU anyway
+        smp, res["power"] = None, f"unavailable ({type(e).__name__})"
+    for s in range(steps):
+        for i, (_, (_, _, fn)) in enumerate(calls):
+            fn()
+            F.fc_mfma_probe_launch(clocks[s * len(calls) + i], iters=16)
+    torch.cuda.synchronize()
     if smp:
-        smp.start()
-    pr = F.fc_mfma_probe(args.probe_iters)
-    probe_clock = smp.stop() if smp else None
-    if smp:
+        smp_res = smp.stop()
         smp.close()
-    rate = pr["flops"] / (pr["ms"] / 1e3)
-    res["mfma_probe"] = {"ms": round(pr["ms"], 3), "tflops": round(rate / 1e12, 2),
-                         "compute_units": pr["compute_units"], "clock": probe_clock,
-                         "counter_ratio": round(pr["counter_ratio"], 4), "wall_clock_mhz": pr["wall_clock_mhz"],
-                         "kernel": "mfma_probe_kernel: 64 v_mfma_f32_16x16x32_bf16 per round, 256 AGPR "
-                                   "accumulators per wave, one wave per SIMD, no loads / LDS / barriers"}
-    pc = probe_clock and probe_clock["clock_mhz_mean"]
-    sc = step_clock and step_clock["clock_mhz_mean"]
-    if pc and sc:
-        per_cu = rate / (pr["compute_units"] * pc * 1e6)  # bf16 flop per clock per CU
-        peak = pr["compute_units"] * per_cu * sc * 1e6 / 1e12
-        res.update({"clock_GHz": round(sc / 1e3, 4), "probe_clock_GHz": round(pc / 1e3, 4),
-                    "flop_per_clock_per_cu": round(per_cu, 1),
-                    "clock_scaled_peak": round(peak, 1),
-                    "frac_clock": round(res["step_pass"]["tflops"] / peak, 4)})
+        res["power"] = {"socket_power_w_mean": smp_res["socket_power_w_mean"], "samples": smp_res["samples"],
+                        "amdsmi_gfxclk_mhz_mean": smp_res["clock_mhz_mean"],
+                        "note": "amdsmi's clock figure is context only: under load it reads below the "
+                                "shader-clock counter and the GRBM counter"}
+    c = clocks.cpu().numpy().astype(np.float64)
+    ghz = ((c[..., 1] - c[..., 0]) / (c[..., 3] - c[..., 2])).mean(axis=1) * wall_mhz / 1e3
+    ghz = ghz.reshape(steps, len(calls))
+    w = np.array([L.g.flops for L, _ in calls], dtype=np.float64)
+    step_ghz = float((ghz.mean(axis=0) * w).sum() / w.sum())
+    res["per_call_clock_GHz"] = {f"{L.g.name} {op}": round(float(v), 4)
+                                 for (L, (op, _, _)), v in zip(calls, ghz.mean(axis=0))}
+    peak = cus * per_cu * step_ghz * 1e9 / 1e12
+    res.update({"clock_GHz": round(step_ghz, 4), "clock_scaled_peak": round(peak, 1),
+                "clock_source": "shader-clock counter / constant-rate counter, read by a short probe launch "
+                                "after every GEMM of a second pass of the step (flop-weighted mean)"})
     return res
 
 
@@ -501,12 +522,13 @@ def main():
     }
 
     if not args.no_clock:
-        result["clock"] = clock_and_probe(layers, args.steps, args, torch, F)
-        c = result["clock"]
-        log(f"clock pass: {c['step_pass']}; probe {c['mfma_probe']['tflops']} TFLOP/s; "
-            f"frac_clock {c.get('frac_clock')}")
-        for k in ("clock_GHz", "clock_scaled_peak", "frac_clock"):
-            result[k] = c.get(k)
+        c = clock_and_probe(layers, args.steps, args, torch, F)
+        result["clock"] = c
+        result["clock_GHz"] = c["clock_GHz"]
+        result["clock_scaled_peak"] = c["clock_scaled_peak"]
+        result["frac_clock"] = round(value / c["clock_scaled_peak"], 4)
+        log(f"clock {c['clock_GHz']} GHz; probe {c['mfma_probe']}; clock-scaled peak {c['clock_scaled_peak']} "
+            f"TFLOP/s; frac_clock {result['frac_clock']}; power {c.get('power')}")
 
     if not args.no_extra:
         del layers

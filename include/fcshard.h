@@ -195,6 +195,17 @@ typedef struct {
 
 fc_status fc_mfma_probe(int64_t iters, fc_mfma_probe_result* out, void* stream);
 
+/*
+ * The same kernel, enqueued on `stream` without waiting: `blocks` blocks (0:
+ * one per compute unit), `iters` rounds. Block b writes four uint64 values
+ * to clocks[4 b .. 4 b + 3] (device memory owned by the caller, 8-byte
+ * aligned, 4 x blocks values): the shader-clock counter at the start and end
+ * of its loop, then the constant-rate counter at the same two points. A
+ * short launch after a GEMM samples the engine clock the GEMM left the chip
+ * at. FC_E_INVALID for a NULL or misaligned buffer or arguments out of range.
+ */
+fc_status fc_mfma_probe_launch(int64_t iters, int blocks, void* clocks, void* stream);
+
 /* static text for a status; never NULL */
 const char* fc_status_str(fc_status status);
 

@@ -11,9 +11,12 @@
 //
 // Each block also reads the shader-clock counter (s_memtime) and the
 // constant-rate counter (s_memrealtime) before and after its loop, so the
-// host can derive the engine clock over the run.
+// host can derive the engine clock over the run. A short launch of it after
+// each GEMM of a step (fc_mfma_probe_launch) samples the clock that the GEMM
+// left the chip at.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstring>
 #include <vector>
 
@@ -26,15 +29,15 @@ namespace {
 constexpr int kProbeMfmaPerIter = 64;
 
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_probe_kernel(
-    int64_t iters, float* sink, unsigned long long* clocks) {
+    int64_t iters, unsigned long long* clocks) {
     const int lane = threadIdx.x & 63;
     f32x4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // operands that depend on the lane, so nothing folds; small values keep
-    // the sums finite
+    // operands that depend on the lane; small values keep the sums finite
+    // (the MFMAs are volatile asm: they run whatever becomes of their results)
     bf16x8 a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -52,12 +55,6 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     w4_acc_drain(acc);
     const unsigned long long t1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
-    sink[(int64_t)blockIdx.x * kW4Threads + threadIdx.x] = s;
     if (threadIdx.x == 0) {
         clocks[4 * blockIdx.x + 0] = t0;
         clocks[4 * blockIdx.x + 1] = t1;
@@ -66,12 +63,20 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     }
 }
 
+fc_status probe_device(int* dev, int* cus, int* wall_khz) {
+    hipDeviceProp_t prop;
+    if (hipGetDevice(dev) != hipSuccess || hipGetDeviceProperties(&prop, *dev) != hipSuccess) return FC_E_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FC_E_UNSUPPORTED;
+    if (hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, *dev) != hipSuccess || *wall_khz <= 0)
+        return FC_E_HIP;
+    *cus = prop.multiProcessorCount;
+    return FC_OK;
+}
+
 struct ProbeBuffers {
-    float* sink = nullptr;
     unsigned long long* clocks = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
     ~ProbeBuffers() {
-        if (sink) (void)hipFree(sink);
         if (clocks) (void)hipFree(clocks);
         for (hipEvent_t e : ev)
             if (e) (void)hipEventDestroy(e);
@@ -83,30 +88,35 @@ struct ProbeBuffers {
 
 using namespace fcs;
 
+extern "C" fc_status fc_mfma_probe_launch(int64_t iters, int blocks, void* clocks, void* stream) {
+    if (!clocks || iters < 1 || iters > ((int64_t)1 << 40) || blocks < 0 || blocks > (1 << 20)) return FC_E_INVALID;
+    if ((uintptr_t)clocks % 8) return FC_E_INVALID;
+    int dev, cus, wall_khz;
+    fc_status st = probe_device(&dev, &cus, &wall_khz);
+    if (st != FC_OK) return st;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks ? blocks : cus), dim3(kW4Threads), 0,
+                       static_cast<hipStream_t>(stream), iters, static_cast<unsigned long long*>(clocks));
+    return hipGetLastError() == hipSuccess ? FC_OK : FC_E_HIP;
+}
+
 extern "C" fc_status fc_mfma_probe(int64_t iters, fc_mfma_probe_result* out, void* stream) {
     if (!out || iters < 1 || iters > ((int64_t)1 << 40)) return FC_E_INVALID;
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return FC_E_HIP;
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FC_E_UNSUPPORTED;
-    int wall_khz = 0;
-    if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wall_khz <= 0)
-        return FC_E_HIP;
-    const int blocks = prop.multiProcessorCount;
+    int dev, blocks, wall_khz;
+    fc_status st = probe_device(&dev, &blocks, &wall_khz);
+    if (st != FC_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     ProbeBuffers b;
-    if (hipMalloc(&b.sink, (size_t)blocks * kW4Threads * sizeof(float)) != hipSuccess ||
-        hipMalloc(&b.clocks, (size_t)blocks * 4 * sizeof(unsigned long long)) != hipSuccess) {
+    if (hipMalloc(&b.clocks, (size_t)blocks * 4 * sizeof(unsigned long long)) != hipSuccess) {
         (void)hipGetLastError();
         return FC_E_NOMEM;
     }
     if (hipEventCreate(&b.ev[0]) != hipSuccess || hipEventCreate(&b.ev[1]) != hipSuccess) return FC_E_HIP;
     // a short warm-up launch, then the timed one
-    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kW4Threads), 0, s, (int64_t)1 + iters / 16, b.sink,
-                       b.clocks);
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kW4Threads), 0, s, (int64_t)1 + iters / 16, b.clocks);
     if (hipEventRecord(b.ev[0], s) != hipSuccess) return FC_E_HIP;
-    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kW4Threads), 0, s, iters, b.sink, b.clocks);
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kW4Threads), 0, s, iters, b.clocks);
     if (hipGetLastError() != hipSuccess || hipEventRecord(b.ev[1], s) != hipSuccess) return FC_E_HIP;
     if (hipEventSynchronize(b.ev[1]) != hipSuccess) return FC_E_HIP;
     float ms = 0.0f;

@@ -72,8 +72,10 @@ def lib() -> ctypes.CDLL:
         L.fc_plans_save.argtypes = [ctypes.c_char_p]
         L.fc_plans_load.argtypes = [ctypes.c_char_p]
         L.fc_mfma_probe.argtypes = [i64, ctypes.POINTER(MfmaProbeResult), vp]
+        L.fc_mfma_probe_launch.argtypes = [i64, ci, vp, vp]
         for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
-                  L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load, L.fc_mfma_probe):
+                  L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load, L.fc_mfma_probe,
+                  L.fc_mfma_probe_launch):
             f.restype = ci
         _lib = L
     return _lib
@@ -236,3 +238,19 @@ def fc_mfma_probe(iters: int = 100000, stream=None) -> dict:
     _check(lib().fc_mfma_probe(int(iters), ctypes.byref(r), _stream(stream)), "fc_mfma_probe")
     return {"ms": r.ms, "flops": r.flops, "compute_units": r.compute_units, "counter_ratio": r.counter_ratio,
             "wall_clock_mhz": r.wall_clock_mhz}
+
+
+def fc_mfma_probe_launch(clocks, iters: int = 16, blocks: int = 0, stream=None) -> None:
+    """Enqueue the MFMA-only kernel without waiting; block b writes its four
+    counter readings to clocks[b] (an int64 CUDA tensor of shape (blocks, 4))."""
+    import torch
+    if not isinstance(clocks, torch.Tensor) or clocks.dtype != torch.int64 or not clocks.is_cuda \
+            or not clocks.is_contiguous() or clocks.dim() != 2 or clocks.shape[1] != 4:
+        raise ValueError("clocks must be a contiguous int64 CUDA tensor of shape (blocks, 4)")
+    n = clocks.shape[0]
+    blocks = int(blocks) or n  # one block per row of clocks by default
+    if blocks > n:
+        raise ValueError(f"clocks holds {n} blocks, {blocks} requested")
+    _one_device(clocks)
+    _check(lib().fc_mfma_probe_launch(int(iters), blocks, clocks.data_ptr(), _stream(stream)),
+           "fc_mfma_probe_launch")
