@@ -71,7 +71,8 @@ typedef enum {
     FC_E_INVALID = 1,     /* NULL pointer, dimension < 1, bad enum, misaligned or overlapping output */
     FC_E_UNSUPPORTED = 2, /* current device is not gfx950, or plan id not applicable */
     FC_E_HIP = 3,         /* a HIP runtime call or kernel launch failed */
-    FC_E_NOMEM = 4        /* workspace or tuning buffers could not be allocated */
+    FC_E_NOMEM = 4,       /* workspace or tuning buffers could not be allocated */
+    FC_E_TOO_LARGE = 5    /* fc_bwd_weight_noalloc: the plan needs more than its static scratch */
 } fc_status;
 
 /* storage order of a LOGICAL matrix */
@@ -113,6 +114,28 @@ fc_status fc_bwd_data(const void* dY, const void* W, fc_order w_order,
  */
 fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY,
                         void* dW, fc_out_dtype dw_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * dW = X^T . dY exactly as fc_bwd_weight (same arguments, same plan, same
+ * bits), for callers that cannot allocate or own no workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It calls no allocating routine: a plan's split-K partial planes, copies or
+ * padded operands go to a static device array of fc_noalloc_scratch_bytes()
+ * bytes (64 MiB) that each device holds from the library's load to the end
+ * of the process, instead of the library's workspace. The plan is the one
+ * fc_bwd_weight would take at this key (tuned, or forced by fc_set_plan,
+ * else the default, which needs no scratch); FC_E_TOO_LARGE if it needs
+ * more scratch than the array holds (e.g. a 4-way split of a dW over 16 Mi
+ * elements). Every call on a device shares that device's array, which keeps
+ * the last call's contents (nothing a plan reads there is left from an
+ * earlier call): calls that can overlap on one device (streams not ordered
+ * by the caller) race on it.
+ */
+fc_status fc_bwd_weight_noalloc(const void* X, fc_order x_order, const void* dY, void* dW,
+                                fc_out_dtype dw_dtype, int64_t M, int64_t K, int64_t N, void* stream);
+
+/* size in bytes of fc_bwd_weight_noalloc's static device scratch */
+int64_t fc_noalloc_scratch_bytes(void);
 
 /*
  * Times candidate plans of all three products at (M, K, N, x_order, w_order,

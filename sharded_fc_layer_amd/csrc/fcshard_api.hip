@@ -189,8 +189,18 @@ struct Key {
     }
 };
 
+// Device scratch of the no-allocation entry point (fc_bwd_weight_noalloc):
+// split-K partial planes, transpose copies or padded operands of its plan.
+// One copy per device, held from the library's load on that device to the
+// end of the process. In host code `scratch` is a host-side stand-in, not
+// the device address: host code only ever uses the address that
+// hipGetSymbolAddress returns for the current device (DevState::scratch).
+constexpr int64_t kNoallocScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
 struct DevState {
     int checked = 0;  // 0 unknown, 1 gfx950, -1 other
+    void* scratch = nullptr;  // this device's copy of `scratch`, once looked up
     char arch[64] = {0};
     void* ws = nullptr;
     int64_t ws_bytes = 0;
@@ -443,6 +453,22 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
 // device synchronization (enqueued kernels may still use it), unless a hot
 // call was captured into a graph while using it: then it is retired and kept
 // until fc_release, so that replays of that graph stay valid.
+// The address of this device's scratch array, looked up once per device
+// with that device current (the caller holds g_mu).
+fc_status scratch_of(int dev, void** out) {
+    DevState& d = g_dev[dev];
+    if (!d.scratch) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return FC_E_HIP;
+        }
+        d.scratch = ptr;
+    }
+    *out = d.scratch;
+    return FC_OK;
+}
+
 fc_status grow_workspace(int dev, int64_t bytes) {
     DevState& d = g_dev[dev];
     if (bytes <= d.ws_bytes) return FC_OK;
@@ -572,6 +598,29 @@ fc_status fc_bwd_weight(const void* X, fc_order x_order, const void* dY, void* d
     return hot_call(FC_OP_BWD_WEIGHT, X, x_order, dY, FC_ROW_MAJOR, dW, dw_dtype, M, K, N, stream, x_order,
                     FC_ROW_MAJOR);
 }
+
+fc_status fc_bwd_weight_noalloc(const void* X, fc_order x_order, const void* dY, void* dW, fc_out_dtype dw_dtype,
+                                int64_t M, int64_t K, int64_t N, void* stream) {
+    if (!X || !dY || !dW) return FC_E_INVALID;
+    Problem p;
+    fc_status st = resolve(FC_OP_BWD_WEIGHT, X, x_order, dY, FC_ROW_MAJOR, dW, dw_dtype, M, K, N, &p);
+    if (st != FC_OK) return st;
+    std::lock_guard<std::mutex> lk(g_mu);  // held until the kernels are enqueued
+    int dev;
+    if ((st = check_device(&dev)) != FC_OK) return st;
+    void* scr = nullptr;
+    if ((st = scratch_of(dev, &scr)) != FC_OK) return st;
+    // the plan fc_bwd_weight would pick at this key, the scratch standing in
+    // for the workspace
+    Plan pl = decode_plan(default_plan(p));
+    auto it = g_plans.find(make_key(dev, FC_OP_BWD_WEIGHT, M, K, N, x_order, FC_ROW_MAJOR, dw_dtype));
+    if (it != g_plans.end() && plan_applies(p, decode_plan(it->second.id))) pl = decode_plan(it->second.id);
+    if (ws_layout(p, pl).total > kNoallocScratchBytes) return FC_E_TOO_LARGE;
+    (void)hipGetLastError();
+    return run_plan(p, pl, scr, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
+}
+
+int64_t fc_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 int fc_plan_count(void) { return kNumPlans; }
 
@@ -834,6 +883,9 @@ const char* fc_status_str(fc_status status) {
         case FC_E_UNSUPPORTED: return "FC_E_UNSUPPORTED: device is not gfx950 or plan does not apply";
         case FC_E_HIP: return "FC_E_HIP: HIP runtime or launch error";
         case FC_E_NOMEM: return "FC_E_NOMEM: device allocation failed";
+        case FC_E_TOO_LARGE:
+            return "FC_E_TOO_LARGE: the plan needs more scratch than the no-allocation entry point's static "
+                   "device buffer holds (fc_noalloc_scratch_bytes)";
     }
     return "unknown fc_status";
 }

@@ -23,7 +23,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fcshard.h")
 ROW, COL = 0, 1                # fc_order
 OUT_BF16, OUT_F32, OUT_F32_ACC = 0, 1, 2  # fc_out_dtype (OUT_F32_ACC: fp32 out += product)
 OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2  # fc_op
-FC_OK, FC_E_INVALID, FC_E_UNSUPPORTED, FC_E_HIP, FC_E_NOMEM = 0, 1, 2, 3, 4
+FC_OK, FC_E_INVALID, FC_E_UNSUPPORTED, FC_E_HIP, FC_E_NOMEM, FC_E_TOO_LARGE = 0, 1, 2, 3, 4, 5
 
 _lib = None
 
@@ -43,7 +43,7 @@ class FcError(RuntimeError):
 def header_functions() -> List[str]:
     """Names of the functions that include/fcshard.h declares."""
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:fc_status|int|const char\*)\s+(fc_\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:fc_status|int|int64_t|const char\*)\s+(fc_\w+)\s*\(", text, re.M)
 
 
 def lib() -> ctypes.CDLL:
@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.fc_fwd.argtypes = [vp, ci, vp, ci, vp, ci, i64, i64, i64, vp]
         L.fc_bwd_data.argtypes = [vp, vp, ci, vp, ci, i64, i64, i64, vp]
         L.fc_bwd_weight.argtypes = [vp, ci, vp, vp, ci, i64, i64, i64, vp]
+        L.fc_bwd_weight_noalloc.argtypes = [vp, ci, vp, vp, ci, i64, i64, i64, vp]
+        L.fc_noalloc_scratch_bytes.argtypes = []
+        L.fc_noalloc_scratch_bytes.restype = i64
         L.fc_tune.argtypes = [i64, i64, i64, ci, ci, ci, ci, vp]
         L.fc_set_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, ci]
         L.fc_plan_describe.argtypes = [ci, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, cs]
@@ -73,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.fc_plans_load.argtypes = [ctypes.c_char_p]
         L.fc_mfma_probe.argtypes = [i64, ctypes.POINTER(MfmaProbeResult), vp]
         L.fc_mfma_probe_launch.argtypes = [i64, ci, vp, vp]
-        for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
+        for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_bwd_weight_noalloc, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
                   L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load, L.fc_mfma_probe,
                   L.fc_mfma_probe_launch):
             f.restype = ci
@@ -184,6 +187,27 @@ def fc_bwd_weight(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16
     _check(lib().fc_bwd_weight(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
                                _stream(stream)), "fc_bwd_weight")
     return dW
+
+
+def fc_bwd_weight_noalloc(X, dY, x_order: int = ROW, out=None, out_dtype: int = OUT_BF16, stream=None):
+    """dW = X^T . dY as fc_bwd_weight, with the plan's staging in the library's
+    static device scratch instead of its workspace (the library allocates
+    nothing; pass out= for a call that allocates nothing at all)."""
+    _bf16_2d(X, "X"), _bf16_2d(dY, "dY")
+    M, K = _logical(X, x_order)
+    M2, N = dY.shape
+    if M2 != M:
+        raise ValueError(f"X is {M}x{K} but dY is {M2}x{N}")
+    dW = _out(out, K, N, out_dtype, X, "out", stream)
+    _one_device(X, dY, dW)
+    _check(lib().fc_bwd_weight_noalloc(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
+                                       _stream(stream)), "fc_bwd_weight_noalloc")
+    return dW
+
+
+def fc_noalloc_scratch_bytes() -> int:
+    """Size of fc_bwd_weight_noalloc's static device scratch."""
+    return int(lib().fc_noalloc_scratch_bytes())
 
 
 def fc_tune(M: int, K: int, N: int, x_order: int = ROW, w_order: int = ROW, out_dtype: int = OUT_BF16,

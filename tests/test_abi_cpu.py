@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol(L):
 def test_enum_values_match_header():
     text = open(F.HEADER).read()
     for name, val in [("FC_OK", F.FC_OK), ("FC_E_INVALID", F.FC_E_INVALID), ("FC_E_UNSUPPORTED", F.FC_E_UNSUPPORTED),
-                      ("FC_E_HIP", F.FC_E_HIP), ("FC_E_NOMEM", F.FC_E_NOMEM), ("FC_ROW_MAJOR", F.ROW),
+                      ("FC_E_HIP", F.FC_E_HIP), ("FC_E_NOMEM", F.FC_E_NOMEM),
+                      ("FC_E_TOO_LARGE", F.FC_E_TOO_LARGE), ("FC_ROW_MAJOR", F.ROW),
                       ("FC_COL_MAJOR", F.COL), ("FC_OUT_BF16", F.OUT_BF16), ("FC_OUT_F32", F.OUT_F32),
                       ("FC_OUT_F32_ACCUMULATE", F.OUT_F32_ACC),
                       ("FC_OP_FWD", F.OP_FWD), ("FC_OP_BWD_DATA", F.OP_BWD_DATA),
@@ -50,7 +51,7 @@ def test_enum_values_match_header():
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert F.status_str(s).startswith("FC_")
     assert F.status_str(99) == "unknown fc_status"
     assert F.fc_plan_count() == 480
@@ -62,6 +63,10 @@ def test_null_and_bad_dimensions_rejected_without_a_device(L):
     assert L.fc_fwd(None, 0, fake, 0, fake, 0, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_bwd_data(fake, None, 0, fake, 0, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_bwd_weight(fake, 0, fake, None, 0, 8, 8, 8, None) == F.FC_E_INVALID
+    assert L.fc_bwd_weight_noalloc(fake, 0, None, fake, 0, 8, 8, 8, None) == F.FC_E_INVALID
+    assert L.fc_bwd_weight_noalloc(a_ := ctypes.c_void_p(0x100000), 0, ctypes.c_void_p(0x200000),
+                                   ctypes.c_void_p(0x300000), 0, 8, 0, 8, None) == F.FC_E_INVALID
+    assert F.fc_noalloc_scratch_bytes() == 64 << 20
     # dimensions < 1 and bad enums are caught before any HIP call
     a, b, c = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
     assert L.fc_fwd(a, 0, b, 0, c, 0, 0, 8, 8, None) == F.FC_E_INVALID
