@@ -20,9 +20,11 @@ namespace {
 // 160 KB LDS, as a ring of three A tiles and two B tiles (32 KB each, one
 // array each). Step 1 of stage t opens with the barrier that certifies stage
 // t + 1 and frees stage t's tiles; it then loads the B tile of stage t + 2
-// (into stage t's B tile) and the A tile of stage t + 3 (into stage t's A
-// tile), so A loads have three steps to land and B loads at least one and a
-// half. The loop body holds one period of six stages with every tile fixed
+// into stage t's B tile. The A tile of stage t + 2 goes into the A tile that
+// stage t - 1 freed, loaded in step 0 of stage t: each step then issues half
+// a stage's loads, spread over the step (w64_load_spread), B loads have about
+// one and a half steps to land and A loads two and a half. The loop body
+// holds one period of six stages with every tile fixed
 // (stage t in A tile t mod 3 and B tile t mod 2), and the control flow stays
 // that one loop. A stage count that is not a multiple of 6 either
 // (HEAD < 0) is padded at the front with virtual stages of zeros (up to five
@@ -34,8 +36,8 @@ namespace {
 // stages, no extra work, and still one control path.
 //
 // NA = 2 mirrors the ring: two A tiles and three B tiles (ta2 is the third B
-// tile), A loads for stage t + 2 and B loads for stage t + 3, so the B
-// operand gets the longer lead.
+// tile); the B tile of stage t + 2 is loaded in step 0 and the A tile in
+// step 1, so the B operand gets the longer lead.
 template <bool A_OC, bool B_OC, bool OUT_F32, int BN, int HEAD, int NA>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4k64r_kernel(
     GemmArgs g) {
@@ -47,6 +49,10 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
     constexpr int kLB = DmaPP<B_OC, BKP, BN>::kInstr;
     constexpr int kFar = NA == 3 ? kLA : kLB;  // loads of the operand with three tiles
+    // loads spread over both steps of a stage, except where that runs out of
+    // registers (both operands output-contiguous at 256 columns: all 16 loads
+    // of a stage in step 1, as w64_load_after places them)
+    constexpr bool kSpread = !(A_OC && B_OC && BN == 256);
     __shared__ __attribute__((aligned(1024))) char ta0[kT];
     __shared__ __attribute__((aligned(1024))) char ta1[kT];
     __shared__ __attribute__((aligned(1024))) char ta2[kT];
@@ -75,10 +81,36 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #define FCR_RA(SIDX) ((SIDX) < 0 ? rza : w.ra)
 #define FCR_RB(SIDX) ((SIDX) < 0 ? rzb : w.rb)
     // 8 TN MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
-    // set NXT; with LOADS, the B tile of stage T + 2 into LB, then the A tile
-    // of stage T + 3 into LA (NA = 2: the A tile of T + 2, then the B tile of
-    // T + 3), placed as w64_read_after / w64_load_after say
-#define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, LA, LB, T)                                              \
+    // set NXT; with LOADS, the loads of stage T + 2 of the operand with three
+    // tiles (FAR) or of the other one (near) into tile L, placed as
+    // w64_read_after / w64_load_spread say
+#define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, FAR, L, T)                                              \
+    {                                                                                                  \
+        constexpr bool load_a_ = (FAR) == (NA == 3);                                                   \
+        const uint32_t so_ = load_a_ ? FCR_STEP_A((T) + 2) : FCR_STEP_B((T) + 2);                      \
+        const __amdgpu_buffer_rsrc_t ro_ = load_a_ ? FCR_RA((T) + 2) : FCR_RB((T) + 2);                \
+        constexpr int nl_ = (LOADS) ? (load_a_ ? kLA : kLB) : 0;                                       \
+        _Pragma("unroll") for (int u = 0; u < 8 * TN; ++u) {                                           \
+            mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], fa[CUR][u / TN]);                          \
+            const int r_ = w64_read_after<TN>(nl_, u);                                                 \
+            if (r_ >= 0 && r_ < 8) {                                                                   \
+                fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
+            } else if (r_ >= 8) {                                                                      \
+                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + (r_ - 8) * MF, KS, lane);   \
+            }                                                                                          \
+            const int l_ = w64_load_spread<TN>(nl_, u);                                                \
+            if (l_ >= 0) {                                                                             \
+                if constexpr (load_a_)                                                                 \
+                    da.issue_one(ro_, L, so_, wave, l_);                                               \
+                else                                                                                   \
+                    db.issue_one(ro_, L, so_, wave, l_);                                               \
+            }                                                                                          \
+        }                                                                                              \
+    }
+    // The same step with all of a stage's loads: the B tile of stage T + NB
+    // into LB, then the A tile of stage T + NA into LA (NA = 2: A first),
+    // placed as w64_load_after says.
+#define FCR_STEP2(CUR, NXT, RA, RB, KS, LOADS, LA, LB, T)                                             \
     {                                                                                                  \
         const uint32_t sb_ = FCR_STEP_B((T) + NB), sa_ = FCR_STEP_A((T) + NA);                         \
         const __amdgpu_buffer_rsrc_t rb_ = FCR_RB((T) + NB), ra_ = FCR_RA((T) + NA);                   \
@@ -105,17 +137,29 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             }                                                                                          \
         }                                                                                              \
     }
-    // stage T with A tile P mod NA and B tile P mod NB (P = T mod 6): step 0,
-    // the barrier (only the loads of the operand with three tiles, issued
-    // last in the last step, may still be in flight), step 1 (reads step 0
-    // of stage T + 1)
+    // stage T with A tile P mod NA and B tile P mod NB (P = T mod 6): step 0
+    // (loads the far operand's tile of stage T + 2, into the tile stage T - 1
+    // freed), the barrier (those loads may still be in flight), step 1 (reads
+    // step 0 of stage T + 1; loads the near operand's tile of stage T + 2 into
+    // the tile stage T frees). Without kSpread: step 0 without loads, the
+    // barrier (the far operand's loads, issued last, may still be in flight),
+    // step 1 with the B tile of stage T + NB and the A tile of stage T + NA,
+    // both into the tiles stage T frees.
+#define FCR_FAR_TILE(I) (NA == 3 ? FCR_TA(I) : FCR_TB(I))
+#define FCR_NEAR_TILE(I) (NA == 3 ? FCR_TB(I) : FCR_TA(I))
 #define FCR_STAGE(P, T)                                                                                \
-    {                                                                                                  \
-        FCR_STEP(0, 1, FCR_TA((P) % NA), FCR_TB((P) % NB), 1, false, ta0, tb0, T)                      \
+    if constexpr (kSpread) {                                                                           \
+        FCR_STEP(0, 1, FCR_TA((P) % NA), FCR_TB((P) % NB), 1, true, true, FCR_FAR_TILE(((P) + 2) % 3), T) \
         waitcnt<kFar, 0>();                                                                            \
         __builtin_amdgcn_s_barrier();                                                                  \
-        FCR_STEP(1, 0, FCR_TA(((P) + 1) % NA), FCR_TB(((P) + 1) % NB), 0, true, FCR_TA((P) % NA),      \
-                 FCR_TB((P) % NB), T)                                                                  \
+        FCR_STEP(1, 0, FCR_TA(((P) + 1) % NA), FCR_TB(((P) + 1) % NB), 0, true, false,                 \
+                 FCR_NEAR_TILE((P) % 2), T)                                                            \
+    } else {                                                                                           \
+        FCR_STEP2(0, 1, FCR_TA((P) % NA), FCR_TB((P) % NB), 1, false, ta0, tb0, T)                     \
+        waitcnt<kFar, 0>();                                                                            \
+        __builtin_amdgcn_s_barrier();                                                                  \
+        FCR_STEP2(1, 0, FCR_TA(((P) + 1) % NA), FCR_TB(((P) + 1) % NB), 0, true, FCR_TA((P) % NA),     \
+                  FCR_TB((P) % NB), T)                                                                 \
     }
 
     if (nkt > 0) {
@@ -126,17 +170,20 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             // -pad .. -1 go first and load through zero-size descriptors, so
             // their tiles hold zeros and their MFMAs add nothing.
             const int pad = (6 - nkt % 6) % 6;
-            // stages -pad, -pad + 1 and the tile of -pad + 2 of the operand
-            // with three tiles; wait for the first; read its step 0
+            // stages -pad and -pad + 1, and without kSpread the far operand's
+            // tile of -pad + 2 (else stage -pad's step 0 loads it); wait for
+            // the first; read its step 0
             da.issue_full(FCR_RA(-pad), ta0, FCR_STEP_A(-pad), wave);
             db.issue_full(FCR_RB(-pad), tb0, FCR_STEP_B(-pad), wave);
             da.issue_full(FCR_RA(1 - pad), ta1, FCR_STEP_A(1 - pad), wave);
             db.issue_full(FCR_RB(1 - pad), tb1, FCR_STEP_B(1 - pad), wave);
-            if constexpr (NA == 3)
-                da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
-            else
-                db.issue_full(FCR_RB(2 - pad), ta2, FCR_STEP_B(2 - pad), wave);
-            waitcnt<kLA + kLB + kFar, 0>();
+            if constexpr (!kSpread) {
+                if constexpr (NA == 3)
+                    da.issue_full(FCR_RA(2 - pad), ta2, FCR_STEP_A(2 - pad), wave);
+                else
+                    db.issue_full(FCR_RB(2 - pad), ta2, FCR_STEP_B(2 - pad), wave);
+            }
+            waitcnt<kLA + kLB + (kSpread ? 0 : kFar), 0>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
@@ -152,19 +199,21 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 FCR_STAGE(5, t + 5)
             }
         } else {
-            // stages 0 .. HEAD - 1 take period positions P0 .. 5; stages 0, 1
-            // and stage 2's tile of the operand with three tiles go to those
-            // positions' tiles
+            // stages 0 .. HEAD - 1 take period positions P0 .. 5; stages 0 and
+            // 1 (without kSpread also stage 2's tile of the operand with three
+            // tiles) go to those positions' tiles
             constexpr int P0 = 6 - HEAD;
             da.issue_full(w.ra, FCR_TA(P0 % NA), FCR_STEP_A(0), wave);
             db.issue_full(w.rb, FCR_TB(P0 % NB), FCR_STEP_B(0), wave);
             da.issue_full(w.ra, FCR_TA((P0 + 1) % NA), FCR_STEP_A(1), wave);
             db.issue_full(w.rb, FCR_TB((P0 + 1) % NB), FCR_STEP_B(1), wave);
-            if constexpr (NA == 3)
-                da.issue_full(w.ra, FCR_TA((P0 + 2) % 3), FCR_STEP_A(2), wave);
-            else
-                db.issue_full(w.rb, FCR_TB((P0 + 2) % 3), FCR_STEP_B(2), wave);
-            waitcnt<kLA + kLB + kFar, 0>();
+            if constexpr (!kSpread) {
+                if constexpr (NA == 3)
+                    da.issue_full(w.ra, FCR_TA((P0 + 2) % 3), FCR_STEP_A(2), wave);
+                else
+                    db.issue_full(w.rb, FCR_TB((P0 + 2) % 3), FCR_STEP_B(2), wave);
+            }
+            waitcnt<kLA + kLB + (kSpread ? 0 : kFar), 0>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -203,6 +252,9 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCR_RA
 #undef FCR_RB
 #undef FCR_STEP
+#undef FCR_STEP2
+#undef FCR_FAR_TILE
+#undef FCR_NEAR_TILE
 #undef FCR_STAGE
     w4_acc_drain(acc);  // the last MFMAs must have written their results before the epilogue reads them
 
