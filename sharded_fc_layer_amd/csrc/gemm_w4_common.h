@@ -77,6 +77,15 @@ __device__ constexpr int w64_load_after(int nl, int u) {
     return (nl > 0 && u % gs == 0 && u / gs < nl) ? u / gs : -1;
 }
 
+// w64_read_after for NR fragment reads (NR <= 8 + TN): one or two after the
+// first MFMAs of the first groups.
+template <int TN>
+__device__ constexpr int w64_read_after_n(int nr, int u) {
+    constexpr int gs = TN / 2, rpg = gs > 2 ? 2 : gs - 1;
+    const int r = rpg * (u / gs) + (u % gs) - 1;
+    return (u % gs != 0 && u % gs <= rpg && r < nr) ? r : -1;
+}
+
 // The ring kernels' placement of NL loads in a step (NL <= 16): spread over
 // the whole step, load l after the first MFMA of group 16 l / NL (the reads
 // keep w64_read_after's places). Half a stage's loads per step and at most

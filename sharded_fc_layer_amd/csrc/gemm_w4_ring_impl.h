@@ -49,10 +49,17 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     constexpr int kLA = DmaPP<A_OC, BKP>::kInstr;
     constexpr int kLB = DmaPP<B_OC, BKP, BN>::kInstr;
     constexpr int kFar = NA == 3 ? kLA : kLB;  // loads of the operand with three tiles
-    // loads spread over both steps of a stage, except where that runs out of
-    // registers (both operands output-contiguous at 256 columns: all 16 loads
-    // of a stage in step 1, as w64_load_after places them)
-    constexpr bool kSpread = !(A_OC && B_OC && BN == 256);
+    // loads spread over both steps of a stage (the schedule without it, all 16
+    // loads of a stage in step 1 as w64_load_after places them, is kept for
+    // comparison)
+    constexpr bool kSpread = true;
+    // Where registers are short (both operands output-contiguous at 256
+    // columns), the A fragments of rows 0 .. kSingleA - 1 are single-buffered:
+    // row i's fragment for the next step is read right after the last MFMA
+    // of this step that uses it (MFMA TN i + TN - 1), into the same registers.
+    // The last of those reads still has 8 - kSingleA rows of MFMAs to finish
+    // before the stage's barrier, which waits for every LDS read.
+    constexpr int kSingleA = (A_OC && B_OC && BN == 256) ? 6 : 0;
     __shared__ __attribute__((aligned(1024))) char ta0[kT];
     __shared__ __attribute__((aligned(1024))) char ta1[kT];
     __shared__ __attribute__((aligned(1024))) char ta2[kT];
@@ -81,9 +88,11 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #define FCR_RA(SIDX) ((SIDX) < 0 ? rza : w.ra)
 #define FCR_RB(SIDX) ((SIDX) < 0 ? rzb : w.rb)
     // 8 TN MFMAs from set CUR; fragment reads of step KS of tiles (RA, RB) into
-    // set NXT; with LOADS, the loads of stage T + 2 of the operand with three
-    // tiles (FAR) or of the other one (near) into tile L, placed as
-    // w64_read_after / w64_load_spread say
+    // set NXT (single-buffered A rows: after their last MFMA; the other A rows
+    // and the B fragments as w64_read_after_n places them); with LOADS, the
+    // loads of stage T + 2 of the operand with three tiles (FAR) or of the
+    // other one (near) into tile L, placed as w64_load_spread says
+#define FCR_FA(SET, I) fa[(I) < kSingleA ? 0 : (SET)][I]
 #define FCR_STEP(CUR, NXT, RA, RB, KS, LOADS, FAR, L, T)                                              \
     {                                                                                                  \
         constexpr bool load_a_ = (FAR) == (NA == 3);                                                   \
@@ -91,12 +100,16 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         const __amdgpu_buffer_rsrc_t ro_ = load_a_ ? FCR_RA((T) + 2) : FCR_RB((T) + 2);                \
         constexpr int nl_ = (LOADS) ? (load_a_ ? kLA : kLB) : 0;                                       \
         _Pragma("unroll") for (int u = 0; u < 8 * TN; ++u) {                                           \
-            mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], fa[CUR][u / TN]);                          \
-            const int r_ = w64_read_after<TN>(nl_, u);                                                 \
-            if (r_ >= 0 && r_ < 8) {                                                                   \
-                fa[NXT][r_] = fragment_mf<A_OC, BKP, MF>(RA, wm0 + r_ * MF, KS, lane);                 \
-            } else if (r_ >= 8) {                                                                      \
-                fb[NXT][r_ - 8] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + (r_ - 8) * MF, KS, lane);   \
+            mfma_agpr(acc[u / TN][u % TN], fb[CUR][u % TN], FCR_FA(CUR, u / TN));                      \
+            if (u % TN == TN - 1 && u / TN < kSingleA)                                                 \
+                FCR_FA(NXT, u / TN) = fragment_mf<A_OC, BKP, MF>(RA, wm0 + (u / TN) * MF, KS, lane);  \
+            const int r_ = w64_read_after_n<TN>(8 - kSingleA + TN, u);                                 \
+            if (r_ >= 0 && r_ < 8 - kSingleA) {                                                        \
+                const int i_ = r_ + kSingleA;                                                          \
+                FCR_FA(NXT, i_) = fragment_mf<A_OC, BKP, MF>(RA, wm0 + i_ * MF, KS, lane);             \
+            } else if (r_ >= 8 - kSingleA) {                                                           \
+                const int j_ = r_ - (8 - kSingleA);                                                    \
+                fb[NXT][j_] = fragment_mf<B_OC, BKP, MF, BN>(RB, wn0 + j_ * MF, KS, lane);             \
             }                                                                                          \
             const int l_ = w64_load_spread<TN>(nl_, u);                                                \
             if (l_ >= 0) {                                                                             \
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             waitcnt<kLA + kLB + (kSpread ? 0 : kFar), 0>();
             __builtin_amdgcn_s_barrier();
 #pragma unroll
-            for (int i = 0; i < 8; ++i) fa[0][i] = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
+            for (int i = 0; i < 8; ++i) FCR_FA(0, i) = fragment_mf<A_OC, BKP, MF>(ta0, wm0 + i * MF, 0, lane);
 #pragma unroll
             for (int j = 0; j < TN; ++j) fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(tb0, wn0 + j * MF, 0, lane);
             w4_acc_fence(acc);
@@ -217,7 +230,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             __builtin_amdgcn_s_barrier();
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                fa[0][i] = fragment_mf<A_OC, BKP, MF>(FCR_TA(P0 % NA), wm0 + i * MF, 0, lane);
+                FCR_FA(0, i) = fragment_mf<A_OC, BKP, MF>(FCR_TA(P0 % NA), wm0 + i * MF, 0, lane);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 fb[0][j] = fragment_mf<B_OC, BKP, MF, BN>(FCR_TB(P0 % NB), wn0 + j * MF, 0, lane);
@@ -252,6 +265,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #undef FCR_RA
 #undef FCR_RB
 #undef FCR_STEP
+#undef FCR_FA
 #undef FCR_STEP2
 #undef FCR_FAR_TILE
 #undef FCR_NEAR_TILE
