@@ -21,8 +21,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 constexpr int kBK = 32;        // reduction values per stage
 constexpr int kStages = 4;     // LDS ring depth
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;       // offset past any operand (< 2 GiB)
 constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
 
@@ -366,9 +364,20 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
 }
 
 // Output tile and reduction slice of this block. Blocks are dealt round robin
-// to the 8 XCDs; the map gives each XCD one contiguous range of tile ids, and
-// walks tiles in groups of kGroupM tile-rows so that the blocks resident on
-// one XCD share A and B panels in its L2.
+// to the 8 XCDs (block b to XCD b mod 8) and start roughly in block order, so
+// the blocks running at one time are a window of consecutive ids. The map
+// makes that window compact in two ways at once:
+//  * across the chip: tiles are walked in super-tiles of 16 x 16 tiles (a
+//    wave of 256 blocks), super-tiles left to right along a band of 16 tile
+//    rows, bands top to bottom. A wave then reads 16 A and 16 B panels, which
+//    the XCDs share through the MALL (each XCD owning its own band instead,
+//    a wave would stream 8 x 12 different panels);
+//  * within an XCD: id mod 8 is the XCD, and in a full super-tile XCD x
+//    takes an 8 x 4 sub-block (rows 8 (x / 4) .., columns 4 (x mod 4) ..), so
+//    its 32 running tiles share 8 A and 4 B panels in its L2.
+// Partial super-tiles at the right and bottom edges split between the XCDs
+// by columns (h rows x w / 8 columns each) or rows when the sizes allow it,
+// else go column by column.
 struct BlockTile {
     int slice;
     int64_t m0, n0;
@@ -376,22 +385,36 @@ struct BlockTile {
 
 template <int BM, int BN>
 __device__ __forceinline__ BlockTile map_block(const GemmArgs& g) {
+    constexpr int S = 16;  // super-tile side, in tiles
     const int nbm = (int)((g.M + BM - 1) / BM);
     const int nbn = (int)((g.N + BN - 1) / BN);
     const int tiles = nbm * nbn;
-    const int total = gridDim.x;
     const int lin = blockIdx.x;
-    const int qq = total / kXcds, rem = total % kXcds;
-    const int xcd = lin % kXcds, loc = lin / kXcds;
-    const int id = xcd * qq + (xcd < rem ? xcd : rem) + loc;
-    const int slice = id / tiles;
-    const int pid = id - slice * tiles;
-    const int per_group = kGroupM * nbn;
-    const int first_m = (pid / per_group) * kGroupM;
-    const int gsz = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int tm = first_m + (pid % per_group) % gsz;
-    const int tn = (pid % per_group) / gsz;
-    return BlockTile{slice, (int64_t)tm * BM, (int64_t)tn * BN};
+    const int slice = lin / tiles;
+    int t = lin - slice * tiles;
+    const int sr = t / (S * nbn);  // band of S tile rows (the last one may be shorter)
+    const int h = (nbm - S * sr) < S ? (nbm - S * sr) : S;
+    t -= sr * S * nbn;
+    const int sc = t / (S * h);  // super-tile in the band (the last one may be narrower)
+    const int w = (nbn - S * sc) < S ? (nbn - S * sc) : S;
+    const int q = t - sc * S * h;  // 0 .. h w - 1
+    const int x = q & 7, k = q >> 3;
+    int r, c;
+    if (h == S && w % 4 == 0) {  // XCD x: rows 8 (x / 4) .. + 8, w / 4 columns
+        r = 8 * (x >> 2) + (k & 7);
+        c = (w >> 2) * (x & 3) + (k >> 3);
+    } else if (w % 8 == 0) {  // XCD x: all h rows, w / 8 columns
+        r = k % h;
+        c = (w >> 3) * x + k / h;
+    } else if (h % 8 == 0) {  // XCD x: h / 8 rows, all w columns
+        const int hx = h >> 3;
+        r = hx * x + k % hx;
+        c = k / hx;
+    } else {
+        r = q % h;
+        c = q / h;
+    }
+    return BlockTile{slice, (int64_t)(S * sr + r) * BM, (int64_t)(S * sc + c) * BN};
 }
 
 }  // namespace

@@ -180,6 +180,33 @@ def test_exact_integer_every_plan(shape):
                 F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, -1)
 
 
+# Output grids of more than 16 x 16 block tiles, so the block map's every
+# case runs: full 16 x 16 super-tiles (an 8 x 4 sub-block per XCD), right
+# edges 2 and 8 tiles wide, bottom bands of 1 and 2 tile rows; with 256- and
+# 192-column tiles (18 and 24 tile columns). Forward (the M x N output) on the
+# ring and two-slot plans, exact on every element.
+@pytest.mark.parametrize("shape", [(4352, 128, 4608), (4608, 128, 4096)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_block_map_large_grids(shape):
+    M, K, N = shape
+    d = I.make_integer_inputs(M, K, N, seed=14)
+    c = Case(d, ROW, ROW)
+    O, _ = c.oracle("fwd")
+    ran = 0
+    for pid in range(F.fc_plan_count()):
+        if F.fc_set_plan(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16, pid) != F.FC_OK:
+            continue
+        desc = F.fc_plan_describe(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16)
+        if not desc["kernel"].startswith("gemm_w4k64") or desc["split"] != 1 or desc["copy"] != 0:
+            continue
+        what = f"fwd {shape} plan={pid} {desc['kernel']} tile={desc['tile']}"
+        log(what)
+        G = host(c.gpu("fwd", F.OUT_BF16))
+        torch.cuda.synchronize()
+        assert_exact(G, O, F.OUT_BF16, what)
+        ran += 1
+    assert ran >= 4
+
+
 def test_default_plans_need_no_workspace():
     """Untuned shapes run a plan that needs no workspace, also where the
     one-wave-per-SIMD kernels could only run the reduction padded (K = 2040 is
