@@ -284,13 +284,9 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
 // Head forms that run out of registers and spill in their main loop are not
 // built; those cases run the padded form: at 256 columns, both operands
-// output-contiguous with three A tiles, and B output-contiguous with three B
-// tiles.
-constexpr bool head_spills(bool a_oc, bool b_oc) {
-    return FCW4_RING_BN == 256 && b_oc && (FCW4_RING_NA == 2 || a_oc);
-}
-#define FCW4_HEAD_SPILLS_RC_OC (FCW4_RING_BN == 256 && FCW4_RING_NA == 2)
-#define FCW4_HEAD_SPILLS_OC_OC (FCW4_RING_BN == 256)
+// output-contiguous with a head of 4 stages.
+constexpr bool head_spills(bool a_oc, bool b_oc, int head) { return FCW4_RING_BN == 256 && a_oc && b_oc && head == 4; }
+#define FCW4_HEAD4_SPILLS_OC_OC (FCW4_RING_BN == 256)
 
 // Explicit instantiations (the host pass emits a launch stub for each): the
 // padded form and the head forms that are built.
@@ -306,26 +302,25 @@ FCW4_RI(false, true, false, -1)
 FCW4_RI(false, true, true, -1)
 FCW4_RI(true, true, false, -1)
 FCW4_RI(true, true, true, -1)
-#if !FCW4_HEAD_SPILLS_RC_OC
 FCW4_RIH(false, true, false)
 FCW4_RIH(false, true, true)
-#endif
-#if !FCW4_HEAD_SPILLS_OC_OC
-FCW4_RIH(true, true, false)
-FCW4_RIH(true, true, true)
+FCW4_RI(true, true, false, 2)
+FCW4_RI(true, true, true, 2)
+#if !FCW4_HEAD4_SPILLS_OC_OC
+FCW4_RI(true, true, false, 4)
+FCW4_RI(true, true, true, 4)
 #endif
 #undef FCW4_RIH
 #undef FCW4_RI3
 #undef FCW4_RI
-#undef FCW4_HEAD_SPILLS_RC_OC
-#undef FCW4_HEAD_SPILLS_OC_OC
+#undef FCW4_HEAD4_SPILLS_OC_OC
 
 // the instance for a head form, or the padded one where no head form is
 // built (the padded form is correct for any stage count); its name as
 // profilers show it
 template <bool AOC, bool BOC, bool F32, int HEAD>
 constexpr W4Kernel ring_entry(const char* name, const char* padded_name) {
-    constexpr bool padded = HEAD < 0 || head_spills(AOC, BOC);
+    constexpr bool padded = HEAD < 0 || head_spills(AOC, BOC, HEAD);
     return W4Kernel{gemm_w4k64r_kernel<AOC, BOC, F32, FCW4_RING_BN, padded ? -1 : HEAD, FCW4_RING_NA>,
                     padded ? padded_name : name};
 }
