@@ -65,17 +65,17 @@ def kernel_source_hash(sources=None) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed counter runs, or None
-    when none were taken for it or the kernel sources changed since."""
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    runs, or None when none were taken for it or the kernel sources changed since."""
     import json as _json
     try:
         with open(TRAFFIC_FILE) as f:
             rec = _json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+    if rec.get("source_hash") != kernel_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel)
+    k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 WORKLOAD_NAMES = {

@@ -10,12 +10,18 @@ scaled by what the same counters read for a plain copy of known size. With
 each kernel's engine clock and MFMA busy fraction, and, with
 SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA operations / 512), the flops the
 hardware executed per launch.
+With --report it writes the three summaries of one workload (kernel trace,
+HBM traffic, MFMA utilisation) into a directory as short text files, each
+with the commands that produced its inputs, and records the traffic figures
+in a JSON file keyed by workload and by a hash of the device sources.
 Usage:
 
   python -m sharded_fc_layer_amd.rocprof_summary RESULTS.db [--by-grid] [--pmc]
   python -m sharded_fc_layer_amd.rocprof_summary --traffic FETCH.db WRITE.db \
       --copy-kernel REGEX --copy-bytes N [--json OUT --workload NAME --source-hash H]
   python -m sharded_fc_layer_amd.rocprof_summary --mfma MFMA.db
+  python -m sharded_fc_layer_amd.rocprof_summary --report DIR --workload NAME --prof-dir P \
+      --source-hash H --json profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -86,6 +92,7 @@ def counter_per_dispatch(db: str, counter: str):
 
 # MI355X: 8 XCDs (one GRBM each), 256 CUs x 4 SIMDs; dense bf16 peak 2.5 PFLOP/s at 2.4 GHz
 XCDS, SIMDS, PEAK_TFLOPS, PEAK_GHZ = 8, 1024, 2500.0, 2.4
+PROBE_MIN_NS = 1_000_000  # probe launches shorter than 1 ms are clock samples
 
 
 def mfma_util(db: str, out=sys.stdout):
@@ -107,6 +114,10 @@ def mfma_util(db: str, out=sys.stdout):
     for k, disps in sorted(per.items()):
         rows = [(c, dur[k][d]) for d, c in disps.items()
                 if c.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c and dur[k][d] > 0]
+        if k.startswith("mfma_probe_kernel"):
+            # the short launches between a step's GEMMs are clock samples, too
+            # short for the counters' clock; only the long probe launches count
+            rows = [(c, d) for c, d in rows if d >= PROBE_MIN_NS]
         # kernels without MFMA work (copies, the split-K sum) are short next to
         # the counters' sampling, so their clock would not mean anything
         if not rows or not any(c["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 for c, _ in rows):
@@ -153,6 +164,162 @@ def traffic(fetch_db: str, write_db: str, copy_kernel: str, copy_bytes: int, out
     return res
 
 
+def _bench_line(path: str):
+    """The JSON line bench.py printed in a run's log (None if there is none)."""
+    import json
+    try:
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith("{") and '"metric"' in line:
+                    return json.loads(line)
+    except OSError:
+        return None
+    return None
+
+
+def analytical_flops(bench: dict):
+    """{kernel: mean 2 M N K per call} from a bench line's per-call plan records."""
+    per = defaultdict(list)
+    for r in (bench or {}).get("plans", []):
+        per[r["kernel"]].append(2 * r["M"] * r["K"] * r["N"])
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def algorithmic_bytes(bench: dict):
+    """{kernel: mean compulsory HBM bytes per call}: both bf16 inputs read once,
+    the bf16 output written once."""
+    per = defaultdict(list)
+    for r in (bench or {}).get("plans", []):
+        per[r["kernel"]].append(2 * (r["M"] * r["K"] + r["K"] * r["N"] + r["M"] * r["N"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def report(out_dir: str, workload: str, number: int, prof: str, source_hash: str, json_path: str = None,
+           copy_kernel: str = "elementwise", copy_bytes: int = 1 << 30):
+    """The three summaries of workload `workload` (bench.py --workload
+    `number`) from the runs under `prof`, named as the commands in each file's
+    header say."""
+    import io
+    import json
+    import os
+    w, tag = workload, f"w{number}"
+    plans = os.path.join(prof, f"plans_{tag}.txt")
+    bench_cmd = f"python3 bench.py --workload {number} --plans {plans}"
+    runs = {
+        "tune": f"{bench_cmd} --no-cpu-baseline --no-extra            # tunes, saves the plans",
+        "trace": f"rocprofv3 --kernel-trace --stats -d {prof} -o trace_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {prof} -o fetch_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra "
+                 f"--no-clock --copy-calibration --steps 5 --warmup 2",
+        "write": f"rocprofv3 --pmc WRITE_SIZE -d {prof} -o write_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra "
+                 f"--no-clock --copy-calibration --steps 5 --warmup 2",
+        "mfma": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                f"GRBM_GUI_ACTIVE -d {prof} -o mfma_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra "
+                f"--steps 5 --warmup 2",
+    }
+    me = "python3 -m sharded_fc_layer_amd.rocprof_summary"
+    trace_bench = _bench_line(os.path.join(prof, f"trace_{tag}.log"))
+    mfma_bench = _bench_line(os.path.join(prof, f"mfma_{tag}.log"))
+    plan_lines = []
+    try:
+        with open(plans) as f:
+            plan_lines = [l.rstrip("\n") for l in f if l.strip()]
+    except OSError:
+        pass
+    n_calls = len((trace_bench or {}).get("plans", []))
+
+    def header(title, keys, tool):
+        h = [f"# {title}, workload {w} ({n_calls} GEMMs per step)", f"# kernel source hash: {source_hash}", "#",
+             "# Commands (run from the repository root on one MI355X; TMPDIR=/tmp):"]
+        h += [f"#   {runs[k]}" for k in keys]
+        h += [f"#   {tool}", "#"]
+        return h
+
+    # kernel trace
+    buf = io.StringIO()
+    summarize(os.path.join(prof, f"trace_{tag}_results.db"), False, buf)
+    lines = header("rocprofv3 kernel trace", ["tune", "trace"],
+                   f"{me} {os.path.join(prof, f'trace_{tag}_results.db')}")
+    lines += ["# The profiled run loads the saved plans, so it contains no tuning launches:",
+              "# warm-up and timed steps, steps with per-call HIP events, and the clock pass (a short",
+              "# mfma_probe_kernel launch after every GEMM, and one long launch of it).",
+              "# The plans (fc_plans_save format: arch op M K N x_order w_order out_dtype plan tuned_ms):"]
+    lines += [f"#   {l}" for l in plan_lines] + ["#"]
+    lines += buf.getvalue().rstrip("\n").splitlines()
+    if trace_bench:
+        lines += ["#", f"# bench.py line of the traced run: value {trace_bench['value']} TFLOP/s, ms_per_step "
+                       f"{trace_bench['ms_per_step']}, roofline kernel {trace_bench['roofline']['kernel']} at "
+                       f"{trace_bench['roofline']['achieved']} TFLOP/s over {trace_bench['roofline']['avg_launch_us']} "
+                       f"us per launch (HIP events)"]
+    with open(os.path.join(out_dir, f"kernel_trace__{w}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # traffic
+    buf = io.StringIO()
+    tr = traffic(os.path.join(prof, f"fetch_{tag}_results.db"), os.path.join(prof, f"write_{tag}_results.db"),
+                 copy_kernel, copy_bytes, buf)
+    lines = header("HBM traffic per launch", ["tune", "fetch", "write"],
+                   f"{me} --report profiles --workload {w} --workload-number {number} --prof-dir {prof} "
+                   f"--source-hash {source_hash} --json profiles/traffic.json")
+    lines += ["# The copy reference is one torch elementwise kernel (out = in * 1) over 2^29 bf16",
+              "# values: it reads and writes exactly 1 GiB. Each counter is scaled by",
+              "# (1 GiB / what it read for that copy). FETCH_SIZE counts L2 misses to the data",
+              "# fabric (MALL or HBM).", "#"]
+    lines += buf.getvalue().rstrip("\n").splitlines()
+    alg = algorithmic_bytes(trace_bench)
+    lines.append("#")
+    for k, rec in sorted(tr["kernels"].items()):
+        if k in alg:
+            lines.append(f"# {k}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch measured vs "
+                         f"{alg[k] / 1e6:.1f} MB algorithmic (A + B read once, C written once) = "
+                         f"{rec['hbm_bytes_per_launch'] / alg[k]:.2f}x")
+    with open(os.path.join(out_dir, f"hbm_traffic__{w}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if json_path:
+        rec = {}
+        try:
+            with open(json_path) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        if rec.get("source_hash") != source_hash or "workloads" not in rec:
+            rec = {"source_hash": source_hash, "workloads": {}}
+        rec["workloads"][w] = tr
+        with open(json_path, "w") as f:
+            json.dump(rec, f, indent=1)
+
+    # MFMA utilisation
+    buf = io.StringIO()
+    mu = mfma_util(os.path.join(prof, f"mfma_{tag}_results.db"), buf)
+    lines = header("rocprofv3 MFMA utilisation", ["tune", "mfma"],
+                   f"{me} --mfma {os.path.join(prof, f'mfma_{tag}_results.db')}")
+    lines += ["# clock_GHz = GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+              "# (1024 SIMDs x engine cycles); implied_TFLOP/s = mfma_busy x 2500 x clock / 2.4 GHz (the dense bf16",
+              "# rate those two allow). Kernels without MFMA work are left out. The counter run serialises",
+              "# dispatches with gaps between them, so clocks run higher and the step slower than in the bench.",
+              "# mfma_probe_kernel is the MFMA-only probe: its launches of 1 ms or more (the bench's warm-up and",
+              "# timed probe); the few-microsecond launches between the GEMMs (clock samples) are left out.", "#"]
+    lines += buf.getvalue().rstrip("\n").splitlines()
+    an = analytical_flops(trace_bench)
+    lines += ["#", "# hardware flop count (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against the analytical 2 M N K per launch",
+              "# (analytical: bench.py's per-call records of the traced run; ratio > 1 is MFMA work on padding)"]
+    for k, r in sorted(mu.items()):
+        if k in an and r.get("hw_flops_per_launch"):
+            lines.append(f"#   {k:<58} analytical {an[k] / 1e9:>10.3f} GFLOP  hardware "
+                         f"{r['hw_flops_per_launch'] / 1e9:>10.3f} GFLOP  ratio {r['hw_flops_per_launch'] / an[k]:.4f}")
+    if mfma_bench:
+        c = mfma_bench.get("clock") or {}
+        pr = c.get("mfma_probe") or {}
+        lines += ["#", f"# bench.py line of the counter run: value {mfma_bench['value']} TFLOP/s, ms_per_step "
+                       f"{mfma_bench['ms_per_step']}"]
+        if pr:
+            lines.append(f"# its MFMA-only probe: {pr.get('tflops')} TFLOP/s, shader-clock counter {pr.get('clock_GHz')} "
+                         f"GHz, {pr.get('flop_per_clock_per_cu')} bf16 flop per clock per CU; step clock "
+                         f"{c.get('clock_GHz')} GHz from the probe launches between the GEMMs")
+    with open(os.path.join(out_dir, f"mfma_util__{w}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db", nargs="?")
@@ -165,8 +332,14 @@ def main():
     ap.add_argument("--json", default=None)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--source-hash", default=None)
+    ap.add_argument("--report", metavar="DIR", default=None)
+    ap.add_argument("--prof-dir", default="gpurun_out/prof")
+    ap.add_argument("--workload-number", type=int, default=5)
     a = ap.parse_args()
-    if a.traffic:
+    if a.report:
+        report(a.report, a.workload, a.workload_number, a.prof_dir, a.source_hash, a.json, a.copy_kernel,
+               a.copy_bytes)
+    elif a.traffic:
         res = traffic(a.traffic[0], a.traffic[1], a.copy_kernel, a.copy_bytes)
         if a.json:
             import json

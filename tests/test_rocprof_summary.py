@@ -78,11 +78,20 @@ def test_mfma_busy_and_clock():
         rows.append((GEMM, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2 * 8192 * 2048 * 2048 / 512, disp, dur))
     rows.append((COPY, "GRBM_GUI_ACTIVE", 8 * 1000.0, 3, 500))
     rows.append((COPY, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0, 3, 500))
+    # the MFMA-only probe: one 2 ms launch (counted) and a 4 us clock sample (left out)
+    PROBE = "void fcs::(anonymous namespace)::mfma_probe_kernel(long, unsigned long long*)"
+    for disp, d, busy_p in ((4, 2_000_000, 0.96), (5, 4_000, 0.1)):
+        cyc = d * 2.3
+        rows.append((PROBE, "GRBM_GUI_ACTIVE", cyc * R.XCDS, disp, d))
+        rows.append((PROBE, "SQ_VALU_MFMA_BUSY_CYCLES", busy_p * R.SIMDS * cyc, disp, d))
     with tempfile.TemporaryDirectory() as d:
         db = os.path.join(d, "m.db")
         _counter_db(db, rows)
         res = R.mfma_util(db, io.StringIO())
-    assert set(res) == {"gemm_w4k64_kernel<false, true, false>"}  # the copy has no MFMA work
+    # the copy has no MFMA work; of the probe only the long launch counts
+    assert set(res) == {"gemm_w4k64_kernel<false, true, false>", "mfma_probe_kernel"}
+    p = res["mfma_probe_kernel"]
+    assert p["dispatches"] == 1 and p["clock_ghz"] == pytest.approx(2.3) and p["mfma_busy"] == pytest.approx(0.96)
     r = res["gemm_w4k64_kernel<false, true, false>"]
     assert r["dispatches"] == 2 and r["avg_us"] == pytest.approx(100.0)
     assert r["clock_ghz"] == pytest.approx(clock) and r["mfma_busy"] == pytest.approx(busy)
