@@ -116,6 +116,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// splitk_reduce into a sub-rectangle of a wider output: 4 values per thread,
+// cols a multiple of 4
+__global__ __launch_bounds__(256) void splitk_reduce_rect_kernel(const float* __restrict__ ws, void* __restrict__ out,
+                                                                 bool out_f32, bool accumulate, int64_t rows,
+                                                                 int64_t cols, int64_t ldc, int splits,
+                                                                 int64_t stride) {
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 >= rows * cols) return;
+    const int64_t r = i4 / cols, c = i4 - r * cols;
+    f32x4 s = *reinterpret_cast<const f32x4*>(ws + i4);
+    for (int k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(ws + k * stride + i4);
+    if (out_f32) {
+        float* o = static_cast<float*>(out) + r * ldc + c;
+        if (accumulate) s = *reinterpret_cast<const f32x4*>(o) + s;
+        *reinterpret_cast<f32x4*>(o) = s;
+    } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + r * ldc + c) =
+            bf16x4{(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+    }
+}
+
 // dst row r = src row r (cols values) then zeros up to ld; 8 values (16 B)
 // per thread and step, grid-stride over rows x ld / 8
 __global__ __launch_bounds__(256) void pad_rows_bf16_kernel(const uint16_t* __restrict__ src,
@@ -173,6 +195,19 @@ hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, bool a
                      ((uintptr_t)out % (out_f32 ? 16 : 8) == 0);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, out, out_f32,
                        out_f32 && accumulate, n, splits, stride, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce_rect(const float* ws, void* out, bool out_f32, bool accumulate, int64_t rows,
+                                     int64_t cols, int64_t ldc, int splits, int64_t stride, hipStream_t stream) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    if (cols % 4 != 0 || ldc < cols || ldc % 4 != 0 || stride % 4 != 0 || (uintptr_t)ws % 16 != 0 ||
+        (uintptr_t)out % (out_f32 ? 16 : 8) != 0)
+        return hipErrorInvalidValue;
+    const int64_t blocks = (rows * cols / 4 + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_reduce_rect_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, out, out_f32,
+                       out_f32 && accumulate, rows, cols, ldc, splits, stride);
     return hipGetLastError();
 }
 

@@ -33,8 +33,10 @@
 namespace fcs {
 namespace {
 
-constexpr int kSplits[] = {1, 2, 4};
-constexpr int kNumSplits = 3;
+// split slot 3: split 2 of the tail only (tail_geometry below)
+constexpr int kSplits[] = {1, 2, 4, 2};
+constexpr int kNumSplits = 4;
+constexpr int kTailSplit = 3;
 constexpr int kNumCopy = 4;      // bit 0: copy A to RC, bit 1: copy B to RC
 // 0: 4-wave pipelined, 1: simple, 2-5: 8-wave ping-pong (256 x 256), variant
 // = family - 2: bit 0 one barrier per stage, bit 1 16x16x32 MFMAs;
@@ -52,7 +54,8 @@ constexpr int kMaxDevices = 64;
 
 struct Plan {
     int tile;
-    int split;   // number of reduction slices requested
+    int split;   // number of reduction slices requested (for tail plans: of the tail)
+    bool tail;   // only the tiles past the last whole wave are split (families 8, 9)
     int copy;    // bit mask
     int family;  // 0 pipelined, 1 simple, 2-5 ping-pong variants (family - 2), 6-9 one wave per SIMD
 };
@@ -60,7 +63,9 @@ struct Plan {
 Plan decode_plan(int id) {
     Plan p;
     p.tile = id % kNumTiles;
-    p.split = kSplits[(id / kNumTiles) % kNumSplits];
+    const int si = (id / kNumTiles) % kNumSplits;
+    p.split = kSplits[si];
+    p.tail = si == kTailSplit;
     p.copy = (id / (kNumTiles * kNumSplits)) % kNumCopy;
     p.family = id / (kNumTiles * kNumSplits * kNumCopy);
     return p;
@@ -89,6 +94,34 @@ bool problem_aligned(const Problem& p) {
 }
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// A tail plan (families 8 and 9; 256-row block tiles): when the output's
+// tiles are more than one wave (256 CUs) but not whole waves, the tiles of
+// the last partial wave, at most 128 of them, either the last tile columns
+// or the last tile rows, run as their own launch with the reduction split in
+// two (fp32 partials, then the fixed-order sum into that part of the
+// output): that wave then takes about half a round instead of a whole one.
+// The rest (whole waves) runs unsplit. main = the output columns (along_n)
+// or rows of the unsplit part.
+struct TailGeo {
+    bool ok, along_n;
+    int64_t main;
+};
+
+int64_t gcd64(int64_t a, int64_t b) { return b ? gcd64(b, a % b) : a; }
+
+TailGeo tail_geometry(const Problem& p, int bn) {
+    TailGeo t{false, false, 0};
+    const int64_t nbm = (p.M + 255) / 256, nbn = (p.N + bn - 1) / bn, tiles = nbm * nbn;
+    if (tiles <= 256 || tiles % 256 == 0) return t;
+    // tile columns (rows) whose count times the rows (columns) is a whole
+    // number of waves, the rest at most 128 tiles
+    const int64_t step_n = 256 / gcd64(nbm, 256), main_n = (nbn - 1) / step_n * step_n;
+    if (main_n > 0 && nbm * (nbn - main_n) <= 128) return TailGeo{true, true, main_n * bn};
+    const int64_t step_m = 256 / gcd64(nbn, 256), main_m = (nbm - 1) / step_m * step_m;
+    if (main_m > 0 && nbn * (nbm - main_m) <= 128) return TailGeo{true, false, main_m * 256};
+    return t;
+}
 
 // Effective reduction slicing: slice length is a multiple of 64.
 void split_geometry(int64_t K, int split, int64_t* k_split, int* slices) {
@@ -129,7 +162,12 @@ WsLayout ws_layout(const Problem& p, const Plan& pl) {
     int64_t ks;
     int slices;
     split_geometry(p.K, pl.split, &ks, &slices);
-    if (slices > 1) {
+    if (pl.tail) {  // partial planes of the tail part only
+        const TailGeo t = tail_geometry(p, w4_bn(pl));
+        const int64_t tail_elems = t.along_n ? p.M * (p.N - t.main) : (p.M - t.main) * p.N;
+        w.p_off = off;
+        off += round_up((int64_t)slices * tail_elems * 4, 256);
+    } else if (slices > 1) {
         w.p_off = off;
         off += round_up((int64_t)slices * p.M * p.N * 4, 256);
     }
@@ -174,6 +212,10 @@ bool plan_applies(const Problem& p, const Plan& pl) {
         int slices;
         split_geometry(p.K, pl.split, &ks, &slices);
         if (slices < 2) return false;
+    }
+    if (pl.tail) {  // the rings, no copies or padding, a tail to split
+        if (pl.family < kFamilyW4 + 2 || pl.copy != 0 || pads_reduction(p, pl)) return false;
+        if (!tail_geometry(p, w4_bn(pl)).ok) return false;
     }
     return true;
 }
@@ -334,9 +376,40 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
     g.K = p.K;
     g.lda = lda;
     g.ldb = ldb;
+    g.ldc = p.N;
     g.k_split = ks;
     g.splits = slices;
     g.accumulate = 0;
+    if (pl.tail) {  // whole waves unsplit, the tail split in two (see tail_geometry)
+        const int bn = w4_bn(pl), variant = pl.family - kFamilyW4;
+        const TailGeo t = tail_geometry(p, bn);
+        const int64_t esz = p.out_f32 ? 4 : 2;
+        GemmArgs gm = g, gt = g;
+        gm.C = p.C;
+        gm.k_split = round_up(p.K, 64);
+        gm.splits = 1;
+        gm.c_split_stride = 0;
+        gm.accumulate = p.accumulate ? 1 : 0;
+        char* ct = static_cast<char*>(p.C);
+        if (t.along_n) {  // the tail is the output columns main .. N - 1
+            gm.N = t.main;
+            gt.N = p.N - t.main;
+            gt.B = p.b_oc ? p.B + t.main : p.B + t.main * ldb;
+            ct += t.main * esz;
+        } else {  // the output rows main .. M - 1
+            gm.M = t.main;
+            gt.M = p.M - t.main;
+            gt.A = p.a_oc ? p.A + t.main : p.A + t.main * lda;
+            ct += t.main * p.N * esz;
+        }
+        if ((e = launch_gemm_w4(variant, bn, p.a_oc, p.b_oc, p.out_f32, gm, s)) != hipSuccess) return e;
+        float* part = reinterpret_cast<float*>(base + w.p_off);
+        gt.C = part;
+        gt.ldc = gt.N;
+        gt.c_split_stride = gt.M * gt.N;
+        if ((e = launch_gemm_w4(variant, bn, p.a_oc, p.b_oc, true, gt, s)) != hipSuccess) return e;
+        return launch_splitk_reduce_rect(part, ct, p.out_f32, p.accumulate, gt.M, gt.N, p.N, slices, gt.M * gt.N, s);
+    }
     if (slices > 1) {  // partial planes, summed (and added to C) by the reduction
         float* part = reinterpret_cast<float*>(base + w.p_off);
         g.C = part;
@@ -501,9 +574,12 @@ std::string describe(const Problem& p, int id) {
     const bool aligned = q.M % 8 == 0 && q.N % 8 == 0 && q.K % 8 == 0 &&
                          (uintptr_t)p.C % 16 == 0 && (q.A == nullptr || (uintptr_t)q.A % 16 == 0) &&
                          (q.B == nullptr || (uintptr_t)q.B % 16 == 0);
-    const bool f32 = slices > 1 ? true : p.out_f32;
+    // a tail plan is named by its main (unsplit) kernel
+    const bool f32 = slices > 1 && !pl.tail ? true : p.out_f32;
+    const int64_t ks_k = pl.tail ? round_up(p.K, 64) : ks;
+    const int slices_k = pl.tail ? 1 : slices;
     const char* kname = pl.family == 0            ? pipe_kernel_name(pl.tile, q.a_oc, q.b_oc, f32)
-                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, w4_bn(pl), q.a_oc, q.b_oc, f32, p.K, ks, slices)
+                        : pl.family >= kFamilyW4  ? w4_kernel_name(pl.family - kFamilyW4, w4_bn(pl), q.a_oc, q.b_oc, f32, p.K, ks_k, slices_k)
                         : pl.family >= 2          ? pingpong_kernel_name(pl.family - 2, q.a_oc, q.b_oc, f32)
                                          : gemm_kernel_name(aligned ? pl.tile : kUnalignedTile, q.a_oc, q.b_oc, f32,
                                                             aligned);
@@ -512,7 +588,13 @@ std::string describe(const Problem& p, int id) {
     const long long pad = pads_reduction(p, pl) ? (long long)round_up(p.K, 64) : 0;
     std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d pad=%lld ws=%lld", id, kname, tname,
                   slices, pl.copy, pad, (long long)ws_layout(p, pl).total);
-    return buf;
+    std::string d = buf;
+    if (pl.tail) {  // the unsplit part's extent: tail=n<columns> or tail=m<rows>
+        const TailGeo t = tail_geometry(p, w4_bn(pl));
+        std::snprintf(buf, sizeof buf, " tail=%c%lld", t.along_n ? 'n' : 'm', (long long)t.main);
+        d += buf;
+    }
+    return d;
 }
 
 // --------------------------------------------------------------- tuning

@@ -13,13 +13,16 @@ namespace fcs {
 // either reduction-contiguous (RC) or output-contiguous (OC):
 //   A RC: A(i, r) = A[i * lda + r]      A OC: A(i, r) = A[r * lda + i]
 //   B RC: B(r, j) = B[j * ldb + r]      B OC: B(r, j) = B[r * ldb + j]
-// C is row-major with leading dimension N (bf16 or fp32).
+// C is row-major (bf16 or fp32) with leading dimension ldc: N, or more when
+// C is a sub-rectangle of a wider output (the one-wave-per-SIMD kernels'
+// epilogues honour ldc; every other kernel is only launched with ldc = N).
 struct GemmArgs {
     const uint16_t* A;
     const uint16_t* B;
     void* C;
     int64_t M, N, K;
     int64_t lda, ldb;
+    int64_t ldc;
     int64_t k_split;         // reduction elements per split slice (multiple of 64)
     int splits;              // number of reduction slices; 1 = no split
     int64_t c_split_stride;  // elements between the slices' fp32 partial outputs
@@ -116,6 +119,12 @@ hipError_t launch_pad_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows
 // fp32; with `accumulate` (fp32 only) out[i] = out[i] + that sum.
 hipError_t launch_splitk_reduce(const float* ws, void* out, bool out_f32, bool accumulate, int64_t n, int splits,
                                 int64_t stride, hipStream_t stream);
+
+// The same sum into a sub-rectangle: out[r * ldc + c] (+)= sum_s ws[s * stride
+// + r * cols + c], r < rows, c < cols (cols a multiple of 4; 16-byte aligned
+// planes; the output 8- or 16-byte aligned).
+hipError_t launch_splitk_reduce_rect(const float* ws, void* out, bool out_f32, bool accumulate, int64_t rows,
+                                     int64_t cols, int64_t ldc, int splits, int64_t stride, hipStream_t stream);
 
 // Deterministic pseudo-random bf16 fill in [-1, 1) (tuning buffers only).
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t stream);

@@ -298,7 +298,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int slice, int64_t
 // 256 B of whole 128-byte lines, with half as many store instructions. The
 // 16-byte chunk index in an LDS row is XOR-swizzled by the row (mod 16):
 // a half-wave's writes (16 rows x 16 B) and a row's reads (16 chunks) then
-// fall on distinct banks. Needs N % 8 == 0 and a 16-byte-aligned C.
+// fall on distinct banks. Needs N % 8 == 0, ldc % 8 == 0 and a 16-byte-aligned C.
 template <int TN>
 __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_t m0, int64_t n0, int wm0, int wn0,
                                                        int lane, const f32x4 (&acc)[8][TN], char* stage) {
@@ -321,7 +321,7 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
         const int64_t m = m0 + wm0 + row, n = n0 + wn0 + ch * 8;
         if (m < g.M && n < g.N && (TN == 8 || ch < 2 * TN))
-            *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.N + n) = v;
+            *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.ldc + n) = v;
     }
 }
 
@@ -355,7 +355,7 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
             f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
             const int64_t m = m0 + wm0 + 64 * h + row, n = n0 + wn0 + 4 * ch;
             if (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN)) {
-                float* c = C + m * g.N + n;
+                float* c = C + m * g.ldc + n;
                 if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
                 *reinterpret_cast<f32x4*>(c) = v;
             }

@@ -54,7 +54,7 @@ def test_status_strings(L):
     for s in range(6):
         assert F.status_str(s).startswith("FC_")
     assert F.status_str(99) == "unknown fc_status"
-    assert F.fc_plan_count() == 480
+    assert F.fc_plan_count() == 640
 
 
 def test_null_and_bad_dimensions_rejected_without_a_device(L):
@@ -80,7 +80,7 @@ def test_null_and_bad_dimensions_rejected_without_a_device(L):
     assert L.fc_fwd(a, 0, b, 0, c, 3, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_fwd(a, 0, b, 0, ctypes.c_void_p(0x100010), 0, 8, 8, 8, None) == F.FC_E_INVALID
     assert L.fc_tune(0, 8, 8, 0, 0, 0, 0, None) == F.FC_E_INVALID
-    assert L.fc_set_plan(0, 8, 8, 8, 0, 0, 0, 480) == F.FC_E_INVALID
+    assert L.fc_set_plan(0, 8, 8, 8, 0, 0, 0, F.fc_plan_count()) == F.FC_E_INVALID
     assert L.fc_plan_describe(0, 8, 8, 8, 0, 0, 0, None, 0) == F.FC_E_INVALID
 
 

@@ -207,6 +207,50 @@ def test_exact_block_map_large_grids(shape):
     assert ran >= 4
 
 
+# Tail plans: output grids of 16 x 20 tiles (the last 4 tile columns split)
+# and 20 x 16 tiles (the last 4 tile rows), for each product (its output is
+# M x N, M x K or K x N); reductions of 1024 (two slices of 8 stages, head
+# forms). Exact for every storage order, bf16 and fp32 outputs and an
+# accumulating output.
+TAIL_CASES = [("fwd", (4096, 1024, 5120)), ("fwd", (5120, 1024, 4096)), ("bwd_data", (4096, 5120, 1024)),
+              ("bwd_weight", (1024, 4096, 5120)), ("bwd_weight", (1024, 5120, 4096))]
+
+
+@pytest.mark.parametrize("op,shape", TAIL_CASES, ids=[f"{o}-{'x'.join(map(str, s))}" for o, s in TAIL_CASES])
+def test_exact_tail_split_plans(op, shape):
+    M, K, N = shape
+    d = I.make_integer_inputs(M, K, N, seed=15)
+    rng = np.random.default_rng(15)
+    O = None
+    ran = 0
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        if O is None:
+            O, S = c.oracle(op)
+        for dt in (F.OUT_BF16, F.OUT_F32, F.OUT_F32_ACC):
+            for pid in range(F.fc_plan_count()):
+                if F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, pid) != F.FC_OK:
+                    continue
+                desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, dt)
+                if "tail" not in desc:
+                    continue
+                what = f"{op} {shape} orders={xo}{wo} dtype={dt} plan={pid} {desc['kernel']} tail={desc['tail']}"
+                log(what)
+                if dt == F.OUT_F32_ACC:
+                    C_old = rng.integers(-64, 65, size=O.shape).astype(np.float32)
+                    want, _ = oracle.accumulate(C_old, O, S)
+                    G = host(gpu_acc(c, op, C_old))
+                    assert_exact(G, want, F.OUT_F32, what)
+                else:
+                    G = host(c.gpu(op, dt))
+                    torch.cuda.synchronize()
+                    assert_exact(G, O, dt, what)
+                ran += 1
+            F.fc_set_plan(op_code(op), M, K, N, xo, wo, dt, -1)
+        del c
+    assert ran >= 8
+
+
 def test_default_plans_need_no_workspace():
     """Untuned shapes run a plan that needs no workspace, also where the
     one-wave-per-SIMD kernels could only run the reduction padded (K = 2040 is
