@@ -66,7 +66,19 @@
 extern "C" {
 #endif
 
-typedef enum {
+/*
+ * In C++ the enums below have int as their fixed underlying type, so that
+ * every int a C caller passes is a value of the type and the library can
+ * refuse the ones it does not know without undefined behaviour. In C they
+ * are plain enums, also of int size.
+ */
+#ifdef __cplusplus
+#define FC_INT_ENUM enum : int
+#else
+#define FC_INT_ENUM enum
+#endif
+
+typedef FC_INT_ENUM {
     FC_OK = 0,
     FC_E_INVALID = 1,     /* NULL pointer, dimension < 1, bad enum, misaligned or overlapping output */
     FC_E_UNSUPPORTED = 2, /* current device is not gfx950, or plan id not applicable */
@@ -76,7 +88,7 @@ typedef enum {
 } fc_status;
 
 /* storage order of a LOGICAL matrix */
-typedef enum { FC_ROW_MAJOR = 0, FC_COL_MAJOR = 1 } fc_order;
+typedef FC_INT_ENUM { FC_ROW_MAJOR = 0, FC_COL_MAJOR = 1 } fc_order;
 
 /*
  * output element type. FC_OUT_F32_ACCUMULATE: the output is fp32 and already
@@ -84,10 +96,10 @@ typedef enum { FC_ROW_MAJOR = 0, FC_COL_MAJOR = 1 } fc_order;
  * per element after the product's own fp32 sum), e.g. to accumulate dW over
  * micro-batches. The output must then be initialised by the caller.
  */
-typedef enum { FC_OUT_BF16 = 0, FC_OUT_F32 = 1, FC_OUT_F32_ACCUMULATE = 2 } fc_out_dtype;
+typedef FC_INT_ENUM { FC_OUT_BF16 = 0, FC_OUT_F32 = 1, FC_OUT_F32_ACCUMULATE = 2 } fc_out_dtype;
 
 /* the three products, for the plan-control calls */
-typedef enum { FC_OP_FWD = 0, FC_OP_BWD_DATA = 1, FC_OP_BWD_WEIGHT = 2 } fc_op;
+typedef FC_INT_ENUM { FC_OP_FWD = 0, FC_OP_BWD_DATA = 1, FC_OP_BWD_WEIGHT = 2 } fc_op;
 
 /*
  * Y[M x N] = X[M x K] . W[K x N]   (forward; reduction over K).
@@ -187,8 +199,11 @@ fc_status fc_plans_save(const char* path);
  * Reads such a file (the time field is optional) and caches, for the current
  * device, every line whose arch matches it, with its time if the line has
  * one (growing the workspace as the plans need). Lines for other
- * archs are skipped. FC_E_INVALID if the file cannot be read or a line is
- * malformed (entries before it stay loaded).
+ * archs, blank lines and lines starting with '#' are skipped. FC_E_INVALID if
+ * the file cannot be read or a line is malformed: fields missing or extra,
+ * a number that is not a plain decimal or is out of range, a time that is
+ * not a non-negative number, or a line of 512 characters or more (entries
+ * before it stay loaded).
  */
 fc_status fc_plans_load(const char* path);
 

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cerrno>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -50,6 +51,8 @@ constexpr int kNumFamilies = 10;
 constexpr int kFamilyW4 = 6;
 constexpr int kNumPlans = kNumTiles * kNumSplits * kNumCopy * kNumFamilies;
 constexpr int64_t kPipeMaxBytes = (int64_t)1 << 31;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;    // largest M, K or N
+constexpr int64_t kMaxElems = (int64_t)1 << 46;  // largest element count of X, W, dY or an output
 constexpr int kMaxDevices = 64;
 
 struct Plan {
@@ -447,7 +450,11 @@ fc_status resolve(int op, const void* P, int p_order, const void* Q, int q_order
     if (op < 0 || op > 2) return FC_E_INVALID;
     if (M < 1 || K < 1 || N < 1) return FC_E_INVALID;
     if (bad_order(p_order) || bad_order(q_order) || bad_dtype(dtype)) return FC_E_INVALID;
-    if (M > (int64_t)1 << 31 || K > (int64_t)1 << 31 || N > (int64_t)1 << 31) return FC_E_INVALID;
+    if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return FC_E_INVALID;
+    // each matrix within kMaxElems elements (the products of two dimensions
+    // fit 64 bits here), so that no byte count, offset or workspace size
+    // derived from these sizes overflows
+    if (M * K > kMaxElems || K * N > kMaxElems || M * N > kMaxElems) return FC_E_INVALID;
     Problem p;
     p.out_f32 = dtype != FC_OUT_BF16;
     p.accumulate = dtype == FC_OUT_F32_ACCUMULATE;
@@ -595,6 +602,67 @@ std::string describe(const Problem& p, int id) {
         d += buf;
     }
     return d;
+}
+
+// ------------------------------------------------------------ plan files
+
+// One line of a plan file: "<arch> <op> <M> <K> <N> <x_order> <w_order>
+// <out_dtype> <plan> [<tuned_ms>]", fields separated by blanks.
+struct PlanLine {
+    char arch[64];
+    int op, xo, wo, f32, id;
+    long long M, K, N;
+    float ms;  // -1 when the line has no time
+};
+
+// a decimal integer within [lo, hi] that ends at a blank or the line's end
+bool parse_int_field(const char** cur, long long lo, long long hi, long long* out) {
+    const char* c = *cur;
+    while (*c == ' ' || *c == '\t') ++c;
+    char* end = nullptr;
+    errno = 0;
+    const long long v = std::strtoll(c, &end, 10);
+    if (end == c || errno == ERANGE || v < lo || v > hi) return false;
+    if (*end != '\0' && *end != ' ' && *end != '\t' && *end != '\n' && *end != '\r') return false;
+    *out = v;
+    *cur = end;
+    return true;
+}
+
+// Parses one line of a plan file: 0 on success, 1 for a blank or comment
+// line (skipped), -1 for a malformed line. Values are checked for range
+// only; whether they name a valid problem and plan is set_plan's decision.
+int parse_plan_line(const char* line, PlanLine* out) {
+    const char* c = line;
+    while (*c == ' ' || *c == '\t') ++c;
+    if (*c == '\0' || *c == '\n' || *c == '\r' || *c == '#') return 1;
+    size_t n = 0;
+    while (c[n] && c[n] != ' ' && c[n] != '\t' && c[n] != '\n' && c[n] != '\r') ++n;
+    if (n == 0 || n >= sizeof out->arch) return -1;
+    std::memcpy(out->arch, c, n);
+    out->arch[n] = '\0';
+    c += n;
+    long long v[8];
+    const long long lim = (long long)1 << 40;
+    const long long lo[8] = {-1000, -lim, -lim, -lim, -1000, -1000, -1000, -1000};
+    const long long hi[8] = {1000, lim, lim, lim, 1000, 1000, 1000, 100000};
+    for (int i = 0; i < 8; ++i)
+        if (!parse_int_field(&c, lo[i], hi[i], &v[i])) return -1;
+    out->op = (int)v[0], out->M = v[1], out->K = v[2], out->N = v[3];
+    out->xo = (int)v[4], out->wo = (int)v[5], out->f32 = (int)v[6], out->id = (int)v[7];
+    out->ms = -1.0f;
+    while (*c == ' ' || *c == '\t') ++c;
+    if (*c != '\0' && *c != '\n' && *c != '\r') {  // the optional time
+        char* end = nullptr;
+        errno = 0;
+        const double ms = std::strtod(c, &end);
+        if (end == c || errno == ERANGE || !(ms >= 0.0 && ms < 1e9)) return -1;
+        out->ms = (float)ms;
+        c = end;
+        while (*c == ' ' || *c == '\t') ++c;
+        if (*c != '\0' && *c != '\n' && *c != '\r') return -1;
+    }
+    return 0;
 }
 
 // --------------------------------------------------------------- tuning
@@ -931,27 +999,29 @@ fc_status fc_plans_load(const char* path) {
     char line[512];
     fc_status result = FC_OK;
     while (std::fgets(line, sizeof line, f)) {
-        char arch[64];
-        int op, xo, wo, f32, id;
-        long long M, K, N;
-        float ms = -1.0f;
-        if (line[0] == '\n' || line[0] == '#') continue;
-        const int n =
-            std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d %f", arch, &op, &M, &K, &N, &xo, &wo, &f32, &id, &ms);
-        if (n != 9 && n != 10) {
+        // a line longer than the buffer is malformed (no plan line comes near it)
+        if (!std::strchr(line, '\n') && !std::feof(f)) {
             result = FC_E_INVALID;
             break;
         }
-        if (std::strcmp(arch, g_dev[dev].arch) != 0) continue;
-        fc_status st = set_plan((fc_op)op, M, K, N, (fc_order)xo, (fc_order)wo, (fc_out_dtype)f32, id);
+        PlanLine pl;
+        const int r = parse_plan_line(line, &pl);
+        if (r == 1) continue;
+        if (r != 0) {
+            result = FC_E_INVALID;
+            break;
+        }
+        if (std::strcmp(pl.arch, g_dev[dev].arch) != 0) continue;
+        fc_status st = set_plan((fc_op)pl.op, pl.M, pl.K, pl.N, (fc_order)pl.xo, (fc_order)pl.wo,
+                                (fc_out_dtype)pl.f32, pl.id);
         if (st != FC_OK) {
             result = st;
             break;
         }
-        if (n == 10 && id >= 0) {
+        if (pl.ms >= 0.0f && pl.id >= 0) {
             std::lock_guard<std::mutex> lk(g_mu);
-            auto it = g_plans.find(make_key(dev, (fc_op)op, M, K, N, xo, wo, f32));
-            if (it != g_plans.end()) it->second.ms = ms;
+            auto it = g_plans.find(make_key(dev, (fc_op)pl.op, pl.M, pl.K, pl.N, pl.xo, pl.wo, pl.f32));
+            if (it != g_plans.end()) it->second.ms = pl.ms;
         }
     }
     std::fclose(f);
