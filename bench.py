@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "sharded_fc_layer_amd", "csrc")
 # every source with device code (the C-ABI layer, fcshard_api.hip, is host code only)
 KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                        if f.endswith((".hip", ".h")) and f != "fcshard_api.hip")
+                        if f.endswith((".hip", ".h", ".inc")) and f != "fcshard_api.hip")
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -137,6 +137,17 @@ class Layer:
             ("bwd_data", F.OP_BWD_DATA, lambda: F.fc_bwd_data(self.dY, self.W, self.wo, out=self.dX)),
             ("bwd_weight", F.OP_BWD_WEIGHT, dw),
         ]
+
+
+    def stamp_args(self, code):
+        """fc_stamped's operands, orders and output for product `code` (None
+        when the step accumulates dW in fp32: the stamped form is bf16 only)."""
+        F = self.F
+        if code == F.OP_FWD:
+            return self.X, self.W, self.xo, self.wo, self.Y
+        if code == F.OP_BWD_DATA:
+            return self.dY, self.W, 0, self.wo, self.dX
+        return None if self.dW32 is not None else (self.X, self.dY, self.xo, 0, self.dW)
 
 
 def make_layers(workload, torch, F, I, host_inputs, xo=0, wo=0):
@@ -281,7 +292,86 @@ def clock_and_probe(layers, steps, args, torch, F):
     res.update({"clock_GHz": round(step_ghz, 4), "clock_scaled_peak": round(peak, 1),
                 "clock_source": "shader-clock counter / constant-rate counter, read by a short probe launch "
                                 "after every GEMM of a second pass of the step (flop-weighted mean)"})
+    ik = stamp_pass(layers, steps, wall_mhz, per_cu, cus, torch, F)
+    if "clock_GHz" in ik:
+        ik["clock_scaled_peak"] = round(cus * per_cu * ik["clock_GHz"] * 1e9 / 1e12, 1)
+    res["in_kernel"] = ik
     return res
+
+
+def stamp_pass(layers, steps, wall_mhz, per_cu, cus, torch, F):
+    """The engine clock and the main-loop cycles inside the GEMM kernels.
+
+    The step runs `steps` more times with every product whose plan has a
+    stamped form issued through fc_stamped_call: the same plan, result and
+    main-loop instruction stream, with each block reading the shader-clock
+    and constant-rate counters at entry and exit and the shader clock around
+    its main loop. Products without a stamped form run as usual. Per product:
+    the clock while its blocks ran, the loop's cycles per 64-value stage
+    against the bare MFMA stream's (4 waves x 128 MFMAs of 16 x 16 x 32 per
+    stage at the probe's flop per clock), and the prologue and epilogue."""
+    import numpy as np
+    calls = step_calls(layers)
+    plan = []
+    for L, (op, code, fn) in calls:
+        a = L.stamp_args(code)
+        bufs, ok = [], False
+        if a is not None:
+            rows, cols = a[4].shape
+            nb = ((rows + 255) // 256) * ((cols + 255) // 256)
+            bufs = [torch.zeros((nb, F.STAMP_SLOTS), dtype=torch.int64, device="cuda") for _ in range(steps)]
+            try:
+                F.fc_stamped(code, a[0], a[1], a[2], a[3], out=a[4], stamps=bufs[0])
+                ok = True
+            except F.FcError as e:
+                if e.status != F.FC_E_UNSUPPORTED:
+                    raise
+        plan.append((L, op, fn, a, bufs, ok))
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for L, op, fn, a, bufs, ok in plan:
+            if ok:
+                F.fc_stamped(F.OP_FWD if op == "fwd" else F.OP_BWD_DATA if op == "bwd_data" else F.OP_BWD_WEIGHT,
+                             a[0], a[1], a[2], a[3], out=a[4], stamps=bufs[s])
+            else:
+                fn()
+    torch.cuda.synchronize()
+    floor = 4 * 128 * 16 * 16 * 32 * 2 / per_cu  # cycles per stage of the bare MFMA stream
+    per_call, w_all, w_ok, clk = {}, 0.0, 0.0, 0.0
+    for L, op, fn, a, bufs, ok in plan:
+        w_all += L.g.flops
+        if not ok:
+            per_call[f"{L.g.name} {op}"] = "no stamped form for its plan"
+            continue
+        host = [b.cpu().numpy() for b in bufs]
+        r = F.summarize_stamps(np.concatenate(host), wall_mhz)
+        per_launch = [F.summarize_stamps(h, wall_mhz, compute_units=cus) for h in host]
+        per_call[f"{L.g.name} {op}"] = {
+            "clock_GHz": round(r["clock_GHz"], 4), "loop_cycles_per_stage": round(r["loop_cycles_per_stage"], 1),
+            "loop_vs_mfma_stream": round(floor / r["loop_cycles_per_stage"], 4),
+            "loop_share_of_block": round(r["stages"] * r["loop_cycles_per_stage"] / r["block_cycles"], 4),
+            "cu_occupancy": round(float(np.mean([x["cu_occupancy"] for x in per_launch])), 4),
+            "launch_span_us": round(float(np.mean([x["launch_span_us"] for x in per_launch])), 2),
+            "stages": r["stages"], "prologue_cycles": round(r["prologue_cycles"]),
+            "epilogue_cycles": round(r["epilogue_cycles"]), "block_cycles": round(r["block_cycles"])}
+        w_ok += L.g.flops
+        clk += L.g.flops * r["clock_GHz"]
+    if w_ok == 0:
+        return {"note": "no product of the step has a stamped form"}
+    loops = [v for v in per_call.values() if isinstance(v, dict)]
+    wts = [L.g.flops for L, op, fn, a, bufs, ok in plan if ok]
+    avg = lambda key: round(float(np.average([v[key] for v in loops], weights=wts)), 4)  # noqa: E731
+    return {
+        "clock_GHz": round(clk / w_ok, 4),
+        "loop_vs_mfma_stream": avg("loop_vs_mfma_stream"),
+        "loop_share_of_block": avg("loop_share_of_block"),
+        "cu_occupancy": avg("cu_occupancy"),
+        "mfma_stream_cycles_per_stage": round(floor, 1),
+        "stamped_flop_fraction": round(w_ok / w_all, 4),
+        "per_call": per_call,
+        "source": "fc_stamped_call: per-block shader-clock / constant-rate counter readings inside the GEMM "
+                  "kernels, flop-weighted over the step's products",
+    }
 
 
 def step_calls(layers):
@@ -358,6 +448,8 @@ def plans_of(layers, F, kern=None):
             d = F.fc_plan_describe(op, g.M, g.K, g.N)
             rec = {"gemm": g.name, "op": opname, "M": g.M, "K": g.K, "N": g.N, "kernel": d["kernel"],
                    "split": d["split"], "copy": d["copy"], "pad": d["pad"]}
+            if "tail" in d:  # the kernel runs the unsplit part; the tail is another launch
+                rec["tail"] = d["tail"]
             ms = by_call.get((g.name, opname))
             if ms:
                 avg = sum(ms) / len(ms)
@@ -527,6 +619,9 @@ def main():
         result["clock_GHz"] = c["clock_GHz"]
         result["clock_scaled_peak"] = c["clock_scaled_peak"]
         result["frac_clock"] = round(value / c["clock_scaled_peak"], 4)
+        if "clock_scaled_peak" in c["in_kernel"]:
+            # the same against the clock measured inside the kernels
+            result["frac_in_kernel_clock"] = round(value / c["in_kernel"]["clock_scaled_peak"], 4)
         log(f"clock {c['clock_GHz']} GHz; probe {c['mfma_probe']}; clock-scaled peak {c['clock_scaled_peak']} "
             f"TFLOP/s; frac_clock {result['frac_clock']}; power {c.get('power')}")
 

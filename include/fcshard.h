@@ -244,6 +244,42 @@ fc_status fc_mfma_probe(int64_t iters, fc_mfma_probe_result* out, void* stream);
  */
 fc_status fc_mfma_probe_launch(int64_t iters, int blocks, void* clocks, void* stream);
 
+/*
+ * Measurement aid: one product with cycle stamps. It runs `op` as the
+ * matching hot call would, with the same plan, the same result and the same
+ * instruction stream in the main loop. The ring kernel writes 8 uint64
+ * values per block to `stamps`, which is device memory owned by the caller,
+ * 8-byte aligned, and at least 64 x blocks bytes (stamp_bytes).
+ *
+ * The values of block b, at stamps[8 b .. 8 b + 7]:
+ *   0  shader-clock counter (s_memtime) at entry
+ *   1  constant-rate counter (s_memrealtime, wall_clock_mhz) at entry
+ *   2  shader-clock counter before the first loads
+ *   3  shader-clock counter once the first two reduction stages have landed
+ *   4  shader-clock counter after the last MFMA
+ *   5  shader-clock counter at exit, after the output is stored
+ *   6  constant-rate counter at exit
+ *   7  the reduction stages (64 values each) the block ran
+ * From these the caller derives the engine clock during the kernel, the
+ * cycles per stage of its main loop, and its prologue and epilogue.
+ *
+ * Arguments are those of the hot call of `op`:
+ *   FC_OP_FWD         P = X (p_order), Q = W (q_order)
+ *   FC_OP_BWD_DATA    P = dY, Q = W (q_order); p_order is not read
+ *   FC_OP_BWD_WEIGHT  P = X (p_order), Q = dY; q_order is not read
+ * *blocks receives the number of blocks.
+ *
+ * Only plans whose product is one ring-kernel launch have a stamped form:
+ * family 8 or 9, 256-column tiles, one reduction slice, no tail split, no
+ * transpose copy, bf16 output. A padded reduction is allowed. Any other plan returns
+ * FC_E_UNSUPPORTED, and nothing is enqueued.
+ * FC_E_INVALID: a NULL, misaligned or too small stamps buffer, or arguments
+ * the hot call would refuse.
+ */
+fc_status fc_stamped_call(fc_op op, const void* P, fc_order p_order, const void* Q, fc_order q_order, void* out,
+                          fc_out_dtype out_dtype, int64_t M, int64_t K, int64_t N, void* stamps,
+                          int64_t stamp_bytes, int64_t* blocks, void* stream);
+
 /* static text for a status; never NULL */
 const char* fc_status_str(fc_status status);
 

@@ -331,7 +331,10 @@ int default_plan(const Problem& p) {
 
 // ------------------------------------------------------------- execution
 
-hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) {
+// With `stamps`, the plan must be stampable (see stampable) and its GEMM
+// runs the stamped ring instance, writing kStampSlots values per block.
+hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s,
+                    unsigned long long* stamps = nullptr) {
     Problem p = p0;
     const WsLayout w = ws_layout(p0, pl);
     char* base = static_cast<char*>(ws);
@@ -427,6 +430,10 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s) 
     g.C = p.C;
     g.c_split_stride = 0;
     g.accumulate = p.accumulate ? 1 : 0;
+    if (stamps) {
+        g.stamps = stamps;
+        return launch_gemm_w4_stamped(pl.family - kFamilyW4, p.a_oc, p.b_oc, g, s);
+    }
     if (pl.family == 0) return launch_gemm_pipe(pl.tile, p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= kFamilyW4) return launch_gemm_w4(pl.family - kFamilyW4, w4_bn(pl), p.a_oc, p.b_oc, p.out_f32, g, s);
     if (pl.family >= 2) return launch_gemm_pingpong(pl.family - 2, p.a_oc, p.b_oc, p.out_f32, g, s);
@@ -495,8 +502,22 @@ Key make_key(int dev, int op, int64_t M, int64_t K, int64_t N, int xo, int wo, i
     return Key{dev, op, M, K, N, xo, wo, dtype};
 }
 
+// Plans whose GEMM has a stamped instance: either ring (three A tiles or
+// three B tiles) with 256-column block tiles, one reduction slice, no tail
+// split or transpose copy (a padded reduction is fine), bf16 output.
+bool stampable(const Problem& p, const Plan& pl) {
+    int64_t ks;
+    int slices;
+    split_geometry(p.K, pl.split, &ks, &slices);
+    return (pl.family == kFamilyW4 + 2 || pl.family == kFamilyW4 + 3) && w4_bn(pl) == 256 && !pl.tail &&
+           slices == 1 && pl.copy == 0 && !p.out_f32;
+}
+
+// A hot call; with `stamps` (measurement aid) the plan must be stampable,
+// else FC_E_UNSUPPORTED before anything is enqueued.
 fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_order, void* out, int dtype,
-                   int64_t M, int64_t K, int64_t N, void* stream, int xo, int wo) {
+                   int64_t M, int64_t K, int64_t N, void* stream, int xo, int wo,
+                   unsigned long long* stamps = nullptr, int64_t stamp_bytes = 0, int64_t* blocks = nullptr) {
     if (!P || !Q || !out) return FC_E_INVALID;
     Problem p;
     fc_status st = resolve(op, P, p_order, Q, q_order, out, dtype, M, K, N, &p);
@@ -517,6 +538,12 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
     // never launch a plan whose workspace is not there
     const int64_t ws_need = ws_layout(p, pl).total;
     if (ws_need > g_dev[dev].ws_bytes) return FC_E_UNSUPPORTED;
+    if (stamps) {
+        if (!stampable(p, pl)) return FC_E_UNSUPPORTED;
+        const int64_t nb = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if (stamp_bytes < nb * kStampSlots * 8) return FC_E_INVALID;
+        if (blocks) *blocks = nb;
+    }
     if (ws_need > 0 && !g_dev[dev].ws_captured) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess &&
@@ -526,7 +553,8 @@ fc_status hot_call(int op, const void* P, int p_order, const void* Q, int q_orde
     // the launchers report hipGetLastError(): drop an error that an earlier,
     // unrelated HIP call of this thread left behind
     (void)hipGetLastError();
-    return run_plan(p, pl, g_dev[dev].ws, static_cast<hipStream_t>(stream)) == hipSuccess ? FC_OK : FC_E_HIP;
+    return run_plan(p, pl, g_dev[dev].ws, static_cast<hipStream_t>(stream), stamps) == hipSuccess ? FC_OK
+                                                                                                : FC_E_HIP;
 }
 
 // A larger workspace replaces the current one. The old one is freed after a
@@ -771,6 +799,21 @@ fc_status fc_bwd_weight_noalloc(const void* X, fc_order x_order, const void* dY,
 }
 
 int64_t fc_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+fc_status fc_stamped_call(fc_op op, const void* P, fc_order p_order, const void* Q, fc_order q_order, void* out,
+                          fc_out_dtype out_dtype, int64_t M, int64_t K, int64_t N, void* stamps,
+                          int64_t stamp_bytes, int64_t* blocks, void* stream) {
+    if (!stamps || !blocks || (uintptr_t)stamps % 8 || stamp_bytes < 0) return FC_E_INVALID;
+    if (op != FC_OP_FWD && op != FC_OP_BWD_DATA && op != FC_OP_BWD_WEIGHT) return FC_E_INVALID;
+    // the orders the product does not read are taken as row-major, as in the hot calls
+    const int po = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : p_order;
+    const int qo = op == FC_OP_BWD_WEIGHT ? FC_ROW_MAJOR : q_order;
+    const int xo = op == FC_OP_BWD_DATA ? FC_ROW_MAJOR : p_order;
+    const int wo = op == FC_OP_BWD_WEIGHT ? FC_ROW_MAJOR : q_order;
+    *blocks = 0;
+    return hot_call(op, P, po, Q, qo, out, out_dtype, M, K, N, stream, xo, wo,
+                    static_cast<unsigned long long*>(stamps), stamp_bytes, blocks);
+}
 
 int fc_plan_count(void) { return kNumPlans; }
 

@@ -27,7 +27,12 @@ struct GemmArgs {
     int splits;              // number of reduction slices; 1 = no split
     int64_t c_split_stride;  // elements between the slices' fp32 partial outputs
     int accumulate;          // 1: fp32 C += product (one slice only); 0: C = product
+    // measurement stamps: when set, the ring kernels (gemm_w4k64r_kernel)
+    // write kStampSlots counter readings per block there (see
+    // gemm_w4_ring_impl.h); every other kernel ignores it
+    unsigned long long* stamps = nullptr;
 };
+constexpr int kStampSlots = 8;
 
 struct TileCfg {
     int bm, bn;        // block tile (output rows x output cols)
@@ -105,6 +110,21 @@ template <>
 W4Kernel w4_ring_kernel<256, 2>(int head, bool a_oc, bool b_oc, bool out_f32);
 template <>
 W4Kernel w4_ring_kernel<192, 2>(int head, bool a_oc, bool b_oc, bool out_f32);
+
+// The ring kernel with measurement stamps (GemmArgs::stamps): 256-column
+// block tiles, NA A tiles (3 or 2), bf16 output; head as for
+// w4_ring_kernel. Defined in gemm_w4_ring256.hip and gemm_w4_ring256b.hip.
+template <int NA>
+W4Kernel w4_ring_stamp_kernel(int head, bool a_oc, bool b_oc);
+template <>
+W4Kernel w4_ring_stamp_kernel<3>(int head, bool a_oc, bool b_oc);
+template <>
+W4Kernel w4_ring_stamp_kernel<2>(int head, bool a_oc, bool b_oc);
+
+// Enqueue that kernel (variant 2 or 3 of launch_gemm_w4, 256 columns): one
+// reduction slice, bf16 output, args.stamps set (kStampSlots values per
+// block, blocks = ceil(M / 256) * ceil(N / 256)).
+hipError_t launch_gemm_w4_stamped(int variant, bool a_oc, bool b_oc, const GemmArgs& args, hipStream_t stream);
 
 // dst (cols x rows, row-major) = transpose of src (rows x cols, row-major), bf16.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

@@ -319,4 +319,16 @@ hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f3
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_w4_stamped(int variant, bool a_oc, bool b_oc, const GemmArgs& args, hipStream_t stream) {
+    if (args.splits != 1 || args.stamps == nullptr || (variant != 2 && variant != 3)) return hipErrorInvalidValue;
+    const int64_t blocks = ((args.M + 255) / 256) * ((args.N + 255) / 256);
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int head = ring_head(args.K, args.k_split, 1);
+    const W4Kernel k = variant == 2 ? w4_ring_stamp_kernel<3>(head, a_oc, b_oc)
+                                    : w4_ring_stamp_kernel<2>(head, a_oc, b_oc);
+    hipLaunchKernelGGL(k.fn, dim3((unsigned)blocks), dim3(kW4Threads), 0, stream, args);
+    return hipGetLastError();
+}
+
 }  // namespace fcs

@@ -76,9 +76,11 @@ def lib() -> ctypes.CDLL:
         L.fc_plans_load.argtypes = [ctypes.c_char_p]
         L.fc_mfma_probe.argtypes = [i64, ctypes.POINTER(MfmaProbeResult), vp]
         L.fc_mfma_probe_launch.argtypes = [i64, ci, vp, vp]
+        L.fc_stamped_call.argtypes = [ci, vp, ci, vp, ci, vp, ci, i64, i64, i64, vp, i64,
+                                      ctypes.POINTER(i64), vp]
         for f in (L.fc_fwd, L.fc_bwd_data, L.fc_bwd_weight, L.fc_bwd_weight_noalloc, L.fc_tune, L.fc_set_plan, L.fc_plan_describe,
                   L.fc_plan_count, L.fc_release, L.fc_plans_save, L.fc_plans_load, L.fc_mfma_probe,
-                  L.fc_mfma_probe_launch):
+                  L.fc_mfma_probe_launch, L.fc_stamped_call):
             f.restype = ci
         _lib = L
     return _lib
@@ -203,6 +205,92 @@ def fc_bwd_weight_noalloc(X, dY, x_order: int = ROW, out=None, out_dtype: int = 
     _check(lib().fc_bwd_weight_noalloc(X.data_ptr(), x_order, dY.data_ptr(), dW.data_ptr(), out_dtype, M, K, N,
                                        _stream(stream)), "fc_bwd_weight_noalloc")
     return dW
+
+
+STAMP_SLOTS = 8  # values per block written by fc_stamped_call
+
+
+def fc_stamped(op: int, A, B, a_order: int = ROW, b_order: int = ROW, out=None, stamps=None, stream=None):
+    """One product with cycle stamps (fc_stamped_call, a measurement aid): the
+    same plan and result as the hot call of `op`, with the ring kernel writing
+    STAMP_SLOTS counter readings per block.
+
+    op = OP_FWD: A = X (a_order), B = W (b_order); OP_BWD_DATA: A = dY, B = W
+    (b_order); OP_BWD_WEIGHT: A = X (a_order), B = dY. The output is bf16.
+    Returns (out, stamps): stamps an int64 CUDA tensor (blocks, STAMP_SLOTS),
+    laid out as fcshard.h describes. Raises FcError with FC_E_UNSUPPORTED when
+    the op's plan has no stamped form (nothing is enqueued then)."""
+    import torch
+    _bf16_2d(A, "A"), _bf16_2d(B, "B")
+    if op == OP_FWD:
+        M, K = _logical(A, a_order)
+        K2, N = _logical(B, b_order)
+        if K2 != K:
+            raise ValueError(f"inner dimensions differ: X is {M}x{K}, W is {K2}x{N}")
+        rows, cols = M, N
+    elif op == OP_BWD_DATA:
+        M, N = A.shape
+        K, N2 = _logical(B, b_order)
+        if N2 != N:
+            raise ValueError(f"dY is {M}x{N} but W is {K}x{N2}")
+        rows, cols = M, K
+    elif op == OP_BWD_WEIGHT:
+        M, K = _logical(A, a_order)
+        M2, N = B.shape
+        if M2 != M:
+            raise ValueError(f"X is {M}x{K} but dY is {M2}x{N}")
+        rows, cols = K, N
+    else:
+        raise ValueError(f"unknown op {op}")
+    C = _out(out, rows, cols, OUT_BF16, A, "out", stream)
+    nb = ((rows + 255) // 256) * ((cols + 255) // 256)
+    if stamps is None:
+        stamps = torch.zeros((nb, STAMP_SLOTS), dtype=torch.int64, device=A.device)
+    if not isinstance(stamps, torch.Tensor) or stamps.dtype != torch.int64 or not stamps.is_cuda \
+            or not stamps.is_contiguous() or stamps.dim() != 2 or stamps.shape[1] != STAMP_SLOTS:
+        raise ValueError(f"stamps must be a contiguous int64 CUDA tensor of shape (blocks, {STAMP_SLOTS})")
+    _one_device(A, B, C, stamps)
+    blocks = ctypes.c_int64(0)
+    _check(lib().fc_stamped_call(op, A.data_ptr(), a_order, B.data_ptr(), b_order, C.data_ptr(), OUT_BF16,
+                                 M, K, N, stamps.data_ptr(), stamps.numel() * 8, ctypes.byref(blocks),
+                                 _stream(stream)), "fc_stamped_call")
+    return C, stamps[:blocks.value]
+
+
+def summarize_stamps(stamps, wall_clock_mhz: float, compute_units: Optional[int] = None) -> dict:
+    """Per-launch figures from fc_stamped_call's stamps (an integer array of
+    shape (blocks, STAMP_SLOTS), on the host): the engine clock while the
+    blocks ran (shader-clock ticks over constant-rate ticks), and the mean
+    cycles of each block's set-up, prologue (the first two stages landing),
+    main loop per reduction stage, and epilogue (the output store).
+
+    With compute_units (the stamps of ONE launch), also the launch's span from
+    its first block's entry to its last block's exit, in microseconds of the
+    constant-rate counter, and the CUs' occupancy: the blocks' summed lifetimes
+    over compute_units x that span (one block per CU at a time)."""
+    import numpy as np
+    s = np.asarray(stamps, dtype=np.float64)
+    if s.ndim != 2 or s.shape[1] != STAMP_SLOTS or s.shape[0] == 0:
+        raise ValueError(f"stamps must have shape (blocks, {STAMP_SLOTS}), blocks >= 1")
+    real = s[:, 6] - s[:, 1]
+    if np.any(real <= 0) or np.any(s[:, 7] <= 0):
+        raise ValueError("stamps without elapsed time or stages")
+    ticks = s[:, 5] - s[:, 0]
+    out = {
+        "blocks": int(s.shape[0]),
+        "clock_GHz": float(ticks.sum() / real.sum() * wall_clock_mhz / 1e3),
+        "setup_cycles": float((s[:, 2] - s[:, 0]).mean()),
+        "prologue_cycles": float((s[:, 3] - s[:, 2]).mean()),
+        "loop_cycles_per_stage": float(((s[:, 4] - s[:, 3]) / s[:, 7]).mean()),
+        "epilogue_cycles": float((s[:, 5] - s[:, 4]).mean()),
+        "block_cycles": float(ticks.mean()),
+        "stages": float(s[:, 7].mean()),
+    }
+    if compute_units:
+        span = float(s[:, 6].max() - s[:, 1].min())
+        out["launch_span_us"] = span / wall_clock_mhz
+        out["cu_occupancy"] = float(real.sum() / (compute_units * span))
+    return out
 
 
 def fc_noalloc_scratch_bytes() -> int:

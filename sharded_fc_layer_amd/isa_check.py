@@ -36,7 +36,7 @@ TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 WRITE_WINDOW = 6   # slots between an AGPR write and an MFMA reading it
 READ_WINDOW = 18   # slots between an MFMA and a non-MFMA access of its result
-ASM_KERNELS = re.compile(r"gemm_w4k64r?_kernel")
+ASM_KERNELS = re.compile(r"gemm_w4k64r?(_stamped)?_kernel")
 
 
 def tools_available() -> bool:

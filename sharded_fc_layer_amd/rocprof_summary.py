@@ -178,20 +178,41 @@ def _bench_line(path: str):
     return None
 
 
+def main_launch_extent(r: dict):
+    """(output rows, output cols, reduction) of the launch that a plan record's
+    kernel names: the whole product, or for a tail-split plan ("tail": "m<rows>"
+    or "n<cols>") its unsplit part, whose launch is the named kernel (the tail
+    runs in another launch)."""
+    M, K, N = r["M"], r["K"], r["N"]
+    rows, cols, red = {"fwd": (M, N, K), "bwd_data": (M, K, N), "bwd_weight": (K, N, M)}[r["op"]]
+    t = r.get("tail")
+    if t:
+        if t[0] == "m":
+            rows = int(t[1:])
+        elif t[0] == "n":
+            cols = int(t[1:])
+        else:
+            raise ValueError(f"bad tail field {t!r}")
+    return rows, cols, red
+
+
 def analytical_flops(bench: dict):
-    """{kernel: mean 2 M N K per call} from a bench line's per-call plan records."""
+    """{kernel: mean 2 M N K per call} from a bench line's per-call plan records
+    (of the kernel's own launch: the unsplit part of a tail-split plan)."""
     per = defaultdict(list)
     for r in (bench or {}).get("plans", []):
-        per[r["kernel"]].append(2 * r["M"] * r["K"] * r["N"])
+        rows, cols, red = main_launch_extent(r)
+        per[r["kernel"]].append(2 * rows * cols * red)
     return {k: sum(v) / len(v) for k, v in per.items()}
 
 
 def algorithmic_bytes(bench: dict):
     """{kernel: mean compulsory HBM bytes per call}: both bf16 inputs read once,
-    the bf16 output written once."""
+    the bf16 output written once (of the kernel's own launch, as above)."""
     per = defaultdict(list)
     for r in (bench or {}).get("plans", []):
-        per[r["kernel"]].append(2 * (r["M"] * r["K"] + r["K"] * r["N"] + r["M"] * r["N"]))
+        rows, cols, red = main_launch_extent(r)
+        per[r["kernel"]].append(2 * (rows * red + red * cols + rows * cols))
     return {k: sum(v) / len(v) for k, v in per.items()}
 
 

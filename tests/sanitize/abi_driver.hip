@@ -105,6 +105,9 @@ void plan_space() {
                                                pl.copy, pl.family) == id,
                                    "plan %d does not round-trip", id);
                             const bool applies = plan_applies(p, pl);
+                            if (stampable(p, pl))
+                                EXPECT(pl.family >= kFamilyW4 + 2 && !pl.tail && pl.copy == 0 && !p.out_f32,
+                                       "stampable plan %d", id);
                             const WsLayout w = ws_layout(p, pl);
                             EXPECT(w.total >= 0 && w.total % 256 == 0 && w.a_off >= 0 && w.b_off >= 0 && w.p_off >= 0 &&
                                        w.a_off <= w.total && w.b_off <= w.total && w.p_off <= w.total,
@@ -213,6 +216,22 @@ void entry_points() {
            "describe empty buffer");
     EXPECT(fc_plans_save(nullptr) == FC_E_INVALID && fc_plans_load(nullptr) == FC_E_INVALID, "null plan file");
     EXPECT(fc_mfma_probe(0, nullptr, nullptr) == FC_E_INVALID, "probe iters 0");
+    int64_t nb = -1;
+    EXPECT(fc_stamped_call(FC_OP_FWD, a, FC_ROW_MAJOR, b, FC_ROW_MAJOR, c, FC_OUT_BF16, 4, 4, 4, nullptr, 64, &nb,
+                           nullptr) == FC_E_INVALID,
+           "stamped call without a buffer");
+    EXPECT(fc_stamped_call(FC_OP_FWD, a, FC_ROW_MAJOR, b, FC_ROW_MAJOR, c, FC_OUT_BF16, 4, 4, 4, buf + 3000, 64,
+                           nullptr, nullptr) == FC_E_INVALID,
+           "stamped call without a block count");
+    EXPECT(fc_stamped_call(FC_OP_FWD, a, FC_ROW_MAJOR, b, FC_ROW_MAJOR, c, FC_OUT_BF16, 4, 4, 4, buf + 3001, 64, &nb,
+                           nullptr) == FC_E_INVALID,
+           "stamped call with a misaligned buffer");
+    EXPECT(fc_stamped_call((fc_op)3, a, FC_ROW_MAJOR, b, FC_ROW_MAJOR, c, FC_OUT_BF16, 4, 4, 4, buf + 3000, 64, &nb,
+                           nullptr) == FC_E_INVALID,
+           "stamped call with op 3");
+    EXPECT(fc_stamped_call(FC_OP_BWD_WEIGHT, a, (fc_order)5, b, FC_ROW_MAJOR, c, FC_OUT_BF16, 4, 4, 4, buf + 3000,
+                           64, &nb, nullptr) == FC_E_INVALID,
+           "stamped call with a bad order");
     EXPECT(fc_mfma_probe_launch(1, -1, buf, nullptr) == FC_E_INVALID, "probe launch blocks < 0");
     if (!device) {
         // with no device, calls that pass validation stop at the device check

@@ -97,3 +97,22 @@ def test_mfma_busy_and_clock():
     assert r["clock_ghz"] == pytest.approx(clock) and r["mfma_busy"] == pytest.approx(busy)
     assert r["implied_tflops"] == pytest.approx(busy * 2500.0 * clock / 2.4)
     assert r["hw_flops_per_launch"] == pytest.approx(2 * 8192 * 2048 * 2048)
+
+
+def test_tail_split_plans_count_only_their_main_launch():
+    # bwd_weight of M=8192 tokens, K=26624, N=4096: output K x N, reduction M;
+    # a tail plan whose unsplit part is the first 24576 output rows
+    rec = {"op": "bwd_weight", "M": 8192, "K": 26624, "N": 4096, "kernel": "k_main", "tail": "m24576"}
+    assert R.main_launch_extent(rec) == (24576, 4096, 8192)
+    whole = dict(rec, kernel="k_whole")
+    del whole["tail"]
+    assert R.main_launch_extent(whole) == (26624, 4096, 8192)
+    fl = R.analytical_flops({"plans": [rec, whole]})
+    assert fl["k_main"] == 2 * 24576 * 4096 * 8192 and fl["k_whole"] == 2 * 26624 * 4096 * 8192
+    by = R.algorithmic_bytes({"plans": [rec]})
+    assert by["k_main"] == 2 * (24576 * 8192 + 8192 * 4096 + 24576 * 4096)
+    # column tails, and the other products' extents
+    assert R.main_launch_extent({"op": "fwd", "M": 8, "K": 16, "N": 32, "tail": "n24"}) == (8, 24, 16)
+    assert R.main_launch_extent({"op": "bwd_data", "M": 8, "K": 16, "N": 32}) == (8, 16, 32)
+    with pytest.raises(ValueError):
+        R.main_launch_extent({"op": "fwd", "M": 8, "K": 16, "N": 32, "tail": "x3"})
