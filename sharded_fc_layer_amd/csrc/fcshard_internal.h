@@ -27,9 +27,9 @@ struct GemmArgs {
     int splits;              // number of reduction slices; 1 = no split
     int64_t c_split_stride;  // elements between the slices' fp32 partial outputs
     int accumulate;          // 1: fp32 C += product (one slice only); 0: C = product
-    // measurement stamps: when set, the ring kernels (gemm_w4k64r_kernel)
-    // write kStampSlots counter readings per block there (see
-    // gemm_w4_ring_impl.h); every other kernel ignores it
+    // measurement stamps: the stamped ring kernel (gemm_w4k64r_stamped_kernel)
+    // writes kStampSlots counter readings per block there (slots described in
+    // gemm_w4_ring_body.inc); every other kernel ignores it
     unsigned long long* stamps = nullptr;
 };
 constexpr int kStampSlots = 8;

@@ -40,8 +40,10 @@
 // is two 32-value steps; the barrier sits before the second: it certifies
 // stage t + 1 (whose first step the wave reads next) and frees stage t's
 // slot for the loads of stage t + 2, which have two steps to land.
-// The ring variant (gemm_w4k64r_kernel) lives in gemm_w4_ring_impl.h,
-// built per block-tile width in gemm_w4_ring256.hip and gemm_w4_ring192.hip.
+// The ring variant (gemm_w4k64r_kernel, and its stamped form) lives in
+// gemm_w4_ring_impl.h with its body in gemm_w4_ring_body.inc, built per
+// block-tile width and tile split in gemm_w4_ring256.hip, gemm_w4_ring192.hip,
+// gemm_w4_ring256b.hip and gemm_w4_ring192b.hip.
 #include <algorithm>
 
 #include "gemm_w4_common.h"
