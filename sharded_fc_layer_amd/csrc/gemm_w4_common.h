@@ -77,18 +77,23 @@ __device__ constexpr int w64_load_after(int nl, int u) {
     return (nl > 0 && u % gs == 0 && u / gs < nl) ? u / gs : -1;
 }
 
-// w64_read_after for NR fragment reads (NR <= 8 + TN): one or two after the
-// first MFMAs of the first groups.
-template <int TN>
+// The ring kernels' placement of NR fragment reads (NR <= 8 + TN) in a step:
+// with SPREAD, one after the second MFMA of each group of TN / 2 (over the
+// step's 16 groups), else one or two after the first MFMAs of the first
+// groups. The rings spread them at 256 columns when an operand is
+// output-contiguous (two transposing reads per fragment): against two per
+// group, 2-3 % fewer main-loop cycles and 1-2.5 % less time; with both
+// operands reduction-contiguous spreading cost about 1 %.
+template <int TN, bool SPREAD = false>
 __device__ constexpr int w64_read_after_n(int nr, int u) {
-    constexpr int gs = TN / 2, rpg = gs > 2 ? 2 : gs - 1;
+    constexpr int gs = TN / 2, rpg = SPREAD ? 1 : gs > 2 ? 2 : gs - 1;
     const int r = rpg * (u / gs) + (u % gs) - 1;
     return (u % gs != 0 && u % gs <= rpg && r < nr) ? r : -1;
 }
 
 // The ring kernels' placement of NL loads in a step (NL <= 16): spread over
 // the whole step, load l after the first MFMA of group 16 l / NL (the reads
-// keep w64_read_after's places). Half a stage's loads per step and at most
+// go after later MFMAs of a group, w64_read_after_n). Half a stage's loads per step and at most
 // one load per group keep the direct-to-LDS load rate of the 4 waves at half
 // of what the texture path moves per clock; all 16 in one step hit that rate
 // and the full address FIFO then blocks the wave's next MFMAs.
