@@ -424,7 +424,9 @@ def run_per_launch(layers, steps, torch, F):
         g = L.g
         desc = F.fc_plan_describe(op, g.M, g.K, g.N)
         key = desc["kernel"]
-        single = desc["split"] == 1 and desc["copy"] == 0
+        # one kernel launch per call: no split (reduce launch), transpose copy,
+        # reduction padding (pad_rows launches) or tail split
+        single = desc["split"] == 1 and desc["copy"] == 0 and desc["pad"] == 0 and "tail" not in desc
         e = out.setdefault(key, {"ms": [], "flops": [], "bytes": [], "single_launch": True})
         e["ms"].append(a.elapsed_time(b))
         e["flops"].append(g.flops)
@@ -565,8 +567,8 @@ def main():
 
     kern = run_per_launch(layers, args.steps, torch, F)
     # the dominant kernel among those whose every call launches that kernel
-    # alone (no transpose copy, no split-K reduction), so that the per-call
-    # events time exactly that kernel
+    # alone (no transpose copy, split-K reduction or reduction padding), so
+    # that the per-call events time exactly that kernel
     single = {k: v for k, v in kern.items() if v["single_launch"]} or kern
     dom = max(single.items(), key=lambda kv: sum(kv[1]["ms"]))
     dname, drec = dom
