@@ -64,9 +64,13 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, grids=None):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter
-    runs, or None when none were taken for it or the kernel sources changed since."""
+    runs, or None when none were taken for it or the kernel sources changed since.
+    With `grids` (the launch grid, in threads, of each of this run's calls of
+    the kernel), the mean over those calls of the counter runs' figure for
+    each grid, so that a kernel several GEMMs share is weighed by this run's
+    own calls; the kernel's overall mean if a grid was not profiled."""
     import json as _json
     try:
         with open(TRAFFIC_FILE) as f:
@@ -76,7 +80,12 @@ def measured_traffic(kernel: str, workload: str):
     if rec.get("source_hash") != kernel_source_hash():
         return None
     k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None:
+        return None
+    by = k.get("by_grid") or {}
+    if grids and all(str(g) in by for g in grids):
+        return sum(by[str(g)]["hbm_bytes_per_launch"] for g in grids) / len(grids)
+    return k.get("hbm_bytes_per_launch")
 
 WORKLOAD_NAMES = {
     1: "single_fc_256x512x2048",
@@ -427,8 +436,12 @@ def run_per_launch(layers, steps, torch, F):
         # one kernel launch per call: no split (reduce launch), transpose copy,
         # reduction padding (pad_rows launches) or tail split
         single = desc["split"] == 1 and desc["copy"] == 0 and desc["pad"] == 0 and "tail" not in desc
-        e = out.setdefault(key, {"ms": [], "flops": [], "bytes": [], "single_launch": True})
+        e = out.setdefault(key, {"ms": [], "flops": [], "bytes": [], "grids": [], "single_launch": True})
         e["ms"].append(a.elapsed_time(b))
+        # launch grid in threads (a single launch: 256 x bn tiles, 256 threads each)
+        rows, cols = {"fwd": (g.M, g.N), "bwd_data": (g.M, g.K), "bwd_weight": (g.K, g.N)}[opname]
+        bn = 192 if desc.get("tile") == "256x192" else 256
+        e["grids"].append(-(-rows // 256) * -(-cols // bn) * 256 if key.startswith("gemm_w4") else None)
         e["flops"].append(g.flops)
         # compulsory HBM bytes: both bf16 inputs once, the bf16 output once
         e["bytes"].append(2 * (g.M * g.K + g.K * g.N + g.M * g.N))
@@ -577,7 +590,7 @@ def main():
     achieved = d_avg_flops / (d_avg_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(dname, WORKLOAD_NAMES[args.workload]), "kernel": dname,
+                "traffic": measured_traffic(dname, WORKLOAD_NAMES[args.workload], drec["grids"]), "kernel": dname,
                 "launches": len(drec["ms"]), "avg_launch_us": round(d_avg_ms * 1e3, 2),
                 "avg_gflop_per_launch": round(d_avg_flops / 1e9, 3),
                 "algorithmic_bytes_per_launch": int(np.mean(drec["bytes"])),

@@ -76,18 +76,28 @@ def summarize_pmc(db: str, out=sys.stdout):
             out.write(f"{k:<66} {c:<22} {len(vals):>10} {sum(vals) / len(vals):>18.1f}\n")
 
 
-def counter_per_dispatch(db: str, counter: str):
-    """{kernel: [value per dispatch]} for one counter (summed over dimensions)."""
+def counter_per_dispatch(db: str, counter: str, by_grid: bool = False):
+    """{kernel: [value per dispatch]} for one counter (summed over dimensions);
+    with by_grid, {kernel: {grid size in threads: [value per dispatch]}}."""
     con = sqlite3.connect(db)
     cur = con.cursor()
     cols = [d[0] for d in cur.execute("select * from counters_collection limit 1").description]
     name_col = "kernel_name" if "kernel_name" in cols else "name"
+    grid_col = "grid_size_x" if "grid_size_x" in cols else "0"
     per = defaultdict(lambda: defaultdict(float))
-    for kname, cname, val, disp in cur.execute(
-            f"select {name_col}, counter_name, value, dispatch_id from counters_collection"):
+    grid = {}
+    for kname, cname, val, disp, gx in cur.execute(
+            f"select {name_col}, counter_name, value, dispatch_id, {grid_col} from counters_collection"):
         if cname == counter:
             per[short(kname)][disp] += float(val)
-    return {k: list(v.values()) for k, v in per.items()}
+            grid[(short(kname), disp)] = int(gx)
+    if not by_grid:
+        return {k: list(v.values()) for k, v in per.items()}
+    out = defaultdict(lambda: defaultdict(list))
+    for k, v in per.items():
+        for disp, val in v.items():
+            out[k][grid[(k, disp)]].append(val)
+    return {k: dict(v) for k, v in out.items()}
 
 
 # MI355X: 8 XCDs (one GRBM each), 256 CUs x 4 SIMDs; dense bf16 peak 2.5 PFLOP/s at 2.4 GHz
@@ -153,13 +163,23 @@ def traffic(fetch_db: str, write_db: str, copy_kernel: str, copy_bytes: int, out
     out.write(f"copy calibration: FETCH_SIZE {max(cf):.0f} KiB, WRITE_SIZE {max(cw):.0f} KiB for "
               f"{copy_bytes / 2**30:.3f} GiB each -> scale fetch {f_scale:.4f}, write {w_scale:.4f}\n")
     out.write(f"{'kernel':<66} {'launches':>8} {'fetch_MB':>10} {'write_MB':>10} {'hbm_MB/launch':>14}\n")
+    fetch_g = counter_per_dispatch(fetch_db, "FETCH_SIZE", by_grid=True)
+    write_g = counter_per_dispatch(write_db, "WRITE_SIZE", by_grid=True)
     for k in sorted(set(fetch) & set(write)):
         if pat.search(k):
             continue
         f = sum(fetch[k]) / len(fetch[k]) * 1024 * f_scale
         w = sum(write[k]) / len(write[k]) * 1024 * w_scale
-        res["kernels"][k] = {"launches": len(fetch[k]), "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
-                             "hbm_bytes_per_launch": f + w}
+        rec = {"launches": len(fetch[k]), "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+               "hbm_bytes_per_launch": f + w, "by_grid": {}}
+        # per launch grid (threads): a kernel that several GEMMs share
+        # gets a figure per GEMM shape
+        for g in sorted(set(fetch_g.get(k, {})) & set(write_g.get(k, {}))):
+            fv, wv = fetch_g[k][g], write_g[k][g]
+            fg = sum(fv) / len(fv) * 1024 * f_scale
+            wg = sum(wv) / len(wv) * 1024 * w_scale
+            rec["by_grid"][str(g)] = {"launches": len(fv), "hbm_bytes_per_launch": fg + wg}
+        res["kernels"][k] = rec
         out.write(f"{k:<66} {len(fetch[k]):>8} {f / 1e6:>10.1f} {w / 1e6:>10.1f} {(f + w) / 1e6:>14.1f}\n")
     return res
 

@@ -49,3 +49,20 @@ def test_traffic_figures_only_for_the_current_device_code(tmp_path, monkeypatch)
     rec["source_hash"] = "0" * 16
     f.write_text(json.dumps(rec))
     assert bench.measured_traffic("k", "w") is None
+
+
+def test_traffic_weighs_this_runs_calls_by_launch_grid(tmp_path, monkeypatch):
+    rec = {"source_hash": bench.kernel_source_hash(),
+           "workloads": {"w": {"kernels": {"k": {"hbm_bytes_per_launch": 300.0,
+                                                 "by_grid": {"1024": {"launches": 1, "hbm_bytes_per_launch": 100.0},
+                                                             "4096": {"launches": 2,
+                                                                      "hbm_bytes_per_launch": 400.0}}}}}}}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("k", "w", [1024, 1024, 4096]) == 200.0
+    assert bench.measured_traffic("k", "w", [4096]) == 400.0
+    # a grid the counter runs did not see, or no grids: the kernel's overall mean
+    assert bench.measured_traffic("k", "w", [1024, 2048]) == 300.0
+    assert bench.measured_traffic("k", "w", [None]) == 300.0
+    assert bench.measured_traffic("k", "w") == 300.0

@@ -116,3 +116,29 @@ def test_tail_split_plans_count_only_their_main_launch():
     assert R.main_launch_extent({"op": "bwd_data", "M": 8, "K": 16, "N": 32}) == (8, 16, 32)
     with pytest.raises(ValueError):
         R.main_launch_extent({"op": "fwd", "M": 8, "K": 16, "N": 32, "tail": "x3"})
+
+
+def test_traffic_per_launch_grid():
+    # two GEMM shapes share one kernel: grids of 1024 and 4096 threads
+    gib = 1 << 30
+
+    def db(path, counter, rows):
+        con = sqlite3.connect(path)
+        con.execute("create table counters_collection (kernel_name text, counter_name text, value real, "
+                    "dispatch_id integer, duration integer, grid_size_x integer)")
+        con.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
+        con.commit()
+        con.close()
+
+    with tempfile.TemporaryDirectory() as d:
+        f, w = os.path.join(d, "f.db"), os.path.join(d, "w.db")
+        db(f, "FETCH_SIZE", [(COPY, "FETCH_SIZE", gib / 1024, 1, 1, 64), (GEMM, "FETCH_SIZE", 100.0, 2, 1, 1024),
+                             (GEMM, "FETCH_SIZE", 300.0, 3, 1, 4096), (GEMM, "FETCH_SIZE", 500.0, 4, 1, 4096)])
+        db(w, "WRITE_SIZE", [(COPY, "WRITE_SIZE", gib / 1024, 1, 1, 64), (GEMM, "WRITE_SIZE", 10.0, 2, 1, 1024),
+                             (GEMM, "WRITE_SIZE", 20.0, 3, 1, 4096), (GEMM, "WRITE_SIZE", 20.0, 4, 1, 4096)])
+        res = R.traffic(f, w, "elementwise", gib, io.StringIO())
+    k = res["kernels"]["gemm_w4k64_kernel<false, true, false>"]
+    assert k["hbm_bytes_per_launch"] == pytest.approx((300 + 50 / 3) * 1024)
+    assert k["by_grid"]["1024"] == {"launches": 1, "hbm_bytes_per_launch": pytest.approx(110 * 1024)}
+    assert k["by_grid"]["4096"]["launches"] == 2
+    assert k["by_grid"]["4096"]["hbm_bytes_per_launch"] == pytest.approx(420 * 1024)
