@@ -255,7 +255,8 @@ fc_status fc_mfma_probe_launch(int64_t iters, int blocks, void* clocks, void* st
  *   0  shader-clock counter (s_memtime) at entry
  *   1  constant-rate counter (s_memrealtime, wall_clock_mhz) at entry
  *   2  shader-clock counter before the first loads
- *   3  shader-clock counter once the first two reduction stages have landed
+ *   3  shader-clock counter once the first reduction stage has landed (the
+ *      second, issued with it, may still be in flight)
  *   4  shader-clock counter after the last MFMA
  *   5  shader-clock counter at exit, after the output is stored
  *   6  constant-rate counter at exit

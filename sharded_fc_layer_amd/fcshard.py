@@ -261,7 +261,7 @@ def summarize_stamps(stamps, wall_clock_mhz: float, compute_units: Optional[int]
     """Per-launch figures from fc_stamped_call's stamps (an integer array of
     shape (blocks, STAMP_SLOTS), on the host): the engine clock while the
     blocks ran (shader-clock ticks over constant-rate ticks), and the mean
-    cycles of each block's set-up, prologue (the first two stages landing),
+    cycles of each block's set-up, prologue (the first stage landing),
     main loop per reduction stage, and epilogue (the output store).
 
     With compute_units (the stamps of ONE launch), also the launch's span from
