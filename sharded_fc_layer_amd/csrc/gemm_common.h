@@ -337,27 +337,40 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
                                                       int wn0, int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
     float* C = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride;
+    const int rq = lane >> 5, ch = lane & 31;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        // an accumulating output: all of this half's old values are loaded
+        // first, so their latencies overlap (loaded one by one between the
+        // stores, each load waited out on its own: the compiler cannot prove
+        // that they do not alias the stores before them)
+        f32x4 old[32];
+        if (g.accumulate) {
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                const int64_t m = m0 + wm0 + 64 * h + 2 * q + rq, n = n0 + wn0 + 4 * ch;
+                old[q] = (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN))
+                             ? *reinterpret_cast<const f32x4*>(C + m * g.ldc + n)
+                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = i * 16 + lr;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int ch = 4 * j + lk;
-                *reinterpret_cast<f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
+                const int c4 = 4 * j + lk;
+                *reinterpret_cast<f32x4*>(stage + row * 512 + ((c4 ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
             }
         }
-        const int rq = lane >> 5, ch = lane & 31;
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             const int row = 2 * q + rq;
             f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
             const int64_t m = m0 + wm0 + 64 * h + row, n = n0 + wn0 + 4 * ch;
             if (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN)) {
-                float* c = C + m * g.ldc + n;
-                if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
-                *reinterpret_cast<f32x4*>(c) = v;
+                if (g.accumulate) v += old[q];
+                *reinterpret_cast<f32x4*>(C + m * g.ldc + n) = v;
             }
         }
     }
