@@ -152,6 +152,19 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
     for (int i = 0; i < TM; ++i) {
         const int64_t m = m0 + wm0 + i * 32 + lr;
         if (m >= g.M) continue;
+        float* crow = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N;
+        // an accumulating output: this row block's old values are loaded
+        // first, so their latencies overlap
+        [[maybe_unused]] f32x4 old[TN][4];
+        if (OUT_F32 && g.accumulate) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int64_t n = n0 + wn0 + j * 32 + grp * 8 + lk * 4;
+                    old[j][grp] = n < g.N ? *reinterpret_cast<const f32x4*>(crow + n) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -161,10 +174,9 @@ __global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmArgs g) {
                 const float v0 = acc[i][j][grp * 4 + 0], v1 = acc[i][j][grp * 4 + 1];
                 const float v2 = acc[i][j][grp * 4 + 2], v3 = acc[i][j][grp * 4 + 3];
                 if (OUT_F32) {
-                    float* c = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride + m * g.N + n;
                     f32x4 v{v0, v1, v2, v3};
-                    if (g.accumulate) v += *reinterpret_cast<const f32x4*>(c);
-                    *reinterpret_cast<f32x4*>(c) = v;
+                    if (g.accumulate) v += old[j][grp];
+                    *reinterpret_cast<f32x4*>(crow + n) = v;
                 } else {
                     __bf16* c = static_cast<__bf16*>(g.C) + m * g.N + n;
                     *reinterpret_cast<bf16x4*>(c) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
