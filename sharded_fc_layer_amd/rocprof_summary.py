@@ -261,6 +261,10 @@ def report(out_dir: str, workload: str, number: int, prof: str, source_hash: str
     me = "python3 -m sharded_fc_layer_amd.rocprof_summary"
     trace_bench = _bench_line(os.path.join(prof, f"trace_{tag}.log"))
     mfma_bench = _bench_line(os.path.join(prof, f"mfma_{tag}.log"))
+    for run, rec in (("trace", trace_bench), ("mfma", mfma_bench)):
+        ran = ((rec or {}).get("config") or {}).get("workload")
+        if ran is not None and ran != w:
+            raise ValueError(f"the {run} run of --workload {number} timed workload {ran!r}, not {w!r}")
     plan_lines = []
     try:
         with open(plans) as f:

@@ -142,3 +142,16 @@ def test_traffic_per_launch_grid():
     assert k["by_grid"]["1024"] == {"launches": 1, "hbm_bytes_per_launch": pytest.approx(110 * 1024)}
     assert k["by_grid"]["4096"]["launches"] == 2
     assert k["by_grid"]["4096"]["hbm_bytes_per_launch"] == pytest.approx(420 * 1024)
+
+
+def test_report_refuses_runs_of_another_workload():
+    """A report names its files by workload: runs of another workload's bench
+    line (a wrong --workload-number) are refused before anything is written."""
+    import json
+    with tempfile.TemporaryDirectory() as d:
+        line = {"metric": "m", "value": 1.0, "config": {"workload": "mlp_up_shard_h12288_2x2x2"}}
+        with open(os.path.join(d, "trace_w2.log"), "w") as f:
+            f.write("noise\n" + json.dumps(line) + "\n")
+        with pytest.raises(ValueError, match="timed workload 'mlp_up_shard_h12288_2x2x2'"):
+            R.report(d, "gpt_block_h2048_t8192", 2, d, "0" * 16)
+        assert sorted(os.listdir(d)) == ["trace_w2.log"]
