@@ -138,12 +138,13 @@ void split_geometry(int64_t K, int split, int64_t* k_split, int* slices) {
     *slices = (int)((K + ks - 1) / ks);
 }
 
-// Families 7-9 run reductions that are not a multiple of 64 by padding:
-// each reduction-contiguous operand is copied to rows of round_up(K, 64)
-// values with zeros past K (its last 64-value stage then reads zeros there),
-// while output-contiguous operands read zeros past row K through their
-// buffer bounds. Plans with a transpose copy do not pad.
-bool pads_reduction(const Problem& p, const Plan& pl) { return pl.family > kFamilyW4 && p.K % 64 != 0; }
+// Family 7 runs reductions that are not a multiple of 64 by padding: each
+// reduction-contiguous operand is copied to rows of round_up(K, 64) values
+// with zeros past K (its last 64-value stage then reads zeros there), while
+// output-contiguous operands read zeros past row K through their buffer
+// bounds. Plans with a transpose copy do not pad. The rings (families 8 and
+// 9) load such a partial stage themselves, chunks past K reading zeros.
+bool pads_reduction(const Problem& p, const Plan& pl) { return pl.family == kFamilyW4 + 1 && p.K % 64 != 0; }
 
 struct WsLayout {
     int64_t a_off, b_off, p_off, total;
@@ -200,6 +201,11 @@ bool plan_applies(const Problem& p, const Plan& pl) {
             if (first % 2 != 0 || last % 2 != 0) return false;
         }
         if (pads_reduction(p, pl) && pl.copy != 0) return false;
+        // a ring runs a partial last stage after at least one whole one (in
+        // the slice that ends the reduction; a tail plan's main launch is
+        // unsplit)
+        if (pl.family >= kFamilyW4 + 2 && p.K % 64 != 0 && (p.K - (int64_t)(slices - 1) * ks < 64 || p.K < 64))
+            return false;
     }
     if (pl.family != 1) {
         const int64_t k_a = pads_reduction(p, pl) && !p.a_oc ? round_up(p.K, 64) : p.K;
@@ -621,8 +627,10 @@ std::string describe(const Problem& p, int id) {
     char buf[512];
     const char* tname = w4_bn(pl) == 192 ? "256x192" : kTiles[aligned ? pl.tile : kUnalignedTile].name;
     const long long pad = pads_reduction(p, pl) ? (long long)round_up(p.K, 64) : 0;
-    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d pad=%lld ws=%lld", id, kname, tname,
-                  slices, pl.copy, pad, (long long)ws_layout(p, pl).total);
+    // the values of a partial last stage that a ring kernel loads itself
+    const long long ktail = pl.family >= kFamilyW4 + 2 ? (long long)(p.K % 64) : 0;
+    std::snprintf(buf, sizeof buf, "plan=%d kernel=%s tile=%s split=%d copy=%d pad=%lld ktail=%lld ws=%lld", id, kname,
+                  tname, slices, pl.copy, pad, ktail, (long long)ws_layout(p, pl).total);
     std::string d = buf;
     if (pl.tail) {  // the unsplit part's extent: tail=n<columns> or tail=m<rows>
         const TailGeo t = tail_geometry(p, w4_bn(pl));

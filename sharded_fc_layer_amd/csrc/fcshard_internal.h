@@ -70,9 +70,11 @@ const char* pingpong_kernel_name(int variant, bool a_oc, bool b_oc, bool out_f32
 // bn / 2 per wave with 16x16x32 MFMAs (gemm_w4.hip; same requirements as
 // launch_gemm_pipe; variant 0: K and slices multiples of 64; variant 1: an
 // even number of 64-value stages per slice). A reduction that is not a
-// multiple of 64 ends with a partial stage: reduction-contiguous operands
-// must then have rows padded with zeros up to the next multiple of 64 (lda
-// / ldb the padded length); output-contiguous ones read zeros past row K.
+// multiple of 64 ends with a partial stage. Variant 1: reduction-contiguous
+// operands must then have rows padded with zeros up to the next multiple of
+// 64 (lda / ldb the padded length); output-contiguous ones read zeros past
+// row K. Variants 2 and 3 load the partial stage themselves, 16-byte chunks
+// past K reading zeros (K a multiple of 8), and need no padding.
 // variant 0: 32-value reduction stages in 4 LDS slots; 1: 64-value stages in
 // 2 slots (whole-cache-line rows for reduction-contiguous operands); 2: the
 // same 64-value stages in a ring of 3 A and 2 B tiles, so each load has about

@@ -3,9 +3,11 @@
 // (sciencestack.ai/paper/2502.08145, Figure 1), bf16 in with fp32
 // accumulation (mlsanity.com/paper/2502.08145, Abstract: bf16 training).
 //
-// Requirements (checked by the caller): M, N multiples of 8, K and the
-// split-K slice length multiples of 64 (128 for the 64-value-stage kernel),
-// 16-byte aligned operands and output, every operand smaller than 2 GiB.
+// Requirements (checked by the caller): M, N, K multiples of 8, the split-K
+// slice length a multiple of 64, K too for the 32-value-stage kernel (the
+// others run a partial last stage: the two-slot kernel on operands padded
+// with zeros, the rings by themselves), 16-byte aligned operands and output,
+// every operand smaller than 2 GiB.
 //
 // Common structure (256 threads = 4 wave64s in a 2 x 2 grid, 256 x 256 tile):
 //  * Each wave owns a 128 x 128 output tile: 8 x 8 blocks of
@@ -282,8 +284,11 @@ const W4Kernel kW4[3][8] = {{FCW4_ALL(FCW4_K, gemm_w4_kernel)}, {FCW4_ALL(FCW4_2
 // The ring kernel's head for this launch: the reduction slices' stage count
 // mod 6 when it is 2 or 4 for every slice and every slice has a whole period
 // after its head, else -1 (pad at the front). The kernel tables map head
-// forms that are not built (they would spill) to the padded form.
+// forms that are not built (they would spill) to the padded form. A
+// reduction that is not a multiple of 64 takes the padded form, which runs
+// its partial last stage in the place of the first virtual stage.
 int ring_head(int64_t K, int64_t k_split, int splits) {
+    if (K % 64 != 0) return -1;
     const int64_t first = (std::min(k_split, K) + 63) / 64;
     const int64_t last = (K - (int64_t)(splits - 1) * k_split + 63) / 64;
     const int r = (int)(first % 6);
@@ -315,6 +320,9 @@ hipError_t launch_gemm_w4(int variant, int bn, bool a_oc, bool b_oc, bool out_f3
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + bn - 1) / bn) * (int64_t)args.splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // a ring's partial last stage must follow a whole one
+    if (variant >= 2 && args.K % 64 != 0 && args.K - (int64_t)(args.splits - 1) * args.k_split < 64)
+        return hipErrorInvalidValue;
     const int head = variant >= 2 ? ring_head(args.K, args.k_split, args.splits) : -1;
     hipLaunchKernelGGL(w4_entry(variant, bn, head, a_oc, b_oc, out_f32).fn, dim3((unsigned)blocks),
                        dim3(kW4Threads), 0, stream, args);
@@ -326,6 +334,7 @@ hipError_t launch_gemm_w4_stamped(int variant, bool a_oc, bool b_oc, const GemmA
     const int64_t blocks = ((args.M + 255) / 256) * ((args.N + 255) / 256);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (args.K % 64 != 0 && args.K < 64) return hipErrorInvalidValue;
     const int head = ring_head(args.K, args.k_split, 1);
     const W4Kernel k = variant == 2 ? w4_ring_stamp_kernel<3>(head, a_oc, b_oc)
                                     : w4_ring_stamp_kernel<2>(head, a_oc, b_oc);

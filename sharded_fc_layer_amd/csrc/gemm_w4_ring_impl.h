@@ -2,8 +2,8 @@
 // width, FCW4_RING_BN (256 or 192), and one split of the five LDS tiles,
 // FCW4_RING_NA A tiles (3 unless set), set by the including source file; each
 // such pair is its own translation unit so that the build compiles them in
-// parallel. Requirements as in gemm_w4.hip (K and split slices multiples of
-// 64).
+// parallel. Requirements as in gemm_w4.hip (K a multiple of 8, split slices
+// multiples of 64).
 #include "gemm_w4_common.h"
 
 #ifndef FCW4_RING_BN
@@ -33,7 +33,11 @@ namespace {
 // one whole period after it; 2 and 4 are built) starts with HEAD
 // straight-line stages that take the last HEAD positions of a period, then
 // runs the periods as a do-while: the padded schedule without its virtual
-// stages, no extra work, and still one control path.
+// stages, no extra work, and still one control path. A reduction range that
+// ends with a partial stage (fewer than 64 values) takes the padded form:
+// that stage goes first, in the place of the first virtual stage (one to six
+// of them), and its loads alone check each 16-byte chunk against the end of
+// the range, so the main loop is the same.
 //
 // NA = 2 mirrors the ring: two A tiles and three B tiles (ta2 is the third B
 // tile); the B tile of stage t + 2 is loaded in step 0 and the A tile in

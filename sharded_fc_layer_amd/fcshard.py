@@ -322,7 +322,7 @@ def fc_plan_describe(op: int, M: int, K: int, N: int, x_order: int = ROW, w_orde
     _check(lib().fc_plan_describe(op, M, K, N, x_order, w_order, out_dtype, buf, 512), "fc_plan_describe")
     text = buf.value.decode()
     d = dict(re.findall(r"(\w+)=(gemm_\w+_kernel<[^>]*>|\S+)", text))
-    for k in ("plan", "split", "copy", "pad", "ws"):
+    for k in ("plan", "split", "copy", "pad", "ktail", "ws"):
         d[k] = int(d[k])
     if "tuned_ms" in d:
         d["tuned_ms"] = float(d["tuned_ms"])

@@ -30,6 +30,8 @@ pytestmark = [pytest.mark.gpu,
 ROW, COL = I.ROW, I.COL
 OPS = ["fwd", "bwd_data", "bwd_weight"]
 ALL_ORDERS = [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)]
+RING = 512  # family 8 (ring, 3 A + 2 B tiles), 256 x 256 tiles, one slice, no copy
+RING_B = 576  # family 9 (the mirrored ring, 2 A + 3 B tiles), otherwise the same
 ELEM_TOL, FRO_TOL = 1e-2, 5e-3
 
 
@@ -150,8 +152,14 @@ def test_exact_power_of_two_scaled_inputs():
 # (reductions of 6 q + 2 or 6 q + 4 64-value stages, q >= 1) in all three
 # products: 10 stages (head of 4) forward, 16 (4) backward-data, 8 (2)
 # backward-weight, and the split slices of 8 + 8 (2) and 4 x 4 (padded).
+# (392, 800, 136): reductions of 12 and 6 whole stages and a partial one,
+# which the ring kernels run in front of five virtual stages (800 = 12 x 64 +
+# 32, 392 = 6 x 64 + 8), and of 2 whole stages and 8 values (136); split
+# slices of 448 + 352 and 256 + 136. (352, 608, 224) has 5 whole stages and a
+# partial one (no virtual stage), (200, 1032, 72) 1 whole stage and 8 values.
 @pytest.mark.parametrize("shape", [(264, 520, 136), (200, 1032, 72), (9, 130, 17), (320, 576, 192),
-                                   (384, 1024, 384), (352, 608, 224), (384, 1024, 328), (512, 640, 1024)],
+                                   (384, 1024, 384), (352, 608, 224), (384, 1024, 328), (512, 640, 1024),
+                                   (392, 800, 136)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_exact_integer_every_plan(shape):
     M, K, N = shape
@@ -210,10 +218,12 @@ def test_exact_block_map_large_grids(shape):
 # Tail plans: output grids of 16 x 20 tiles (the last 4 tile columns split)
 # and 20 x 16 tiles (the last 4 tile rows), for each product (its output is
 # M x N, M x K or K x N); reductions of 1024 (two slices of 8 stages, head
-# forms). Exact for every storage order, bf16 and fp32 outputs and an
-# accumulating output.
+# forms) and of 1000 (15 whole stages and 40 values unsplit; slices of 512 and
+# 488 values, the second ending with a partial stage). Exact for every
+# storage order, bf16 and fp32 outputs and an accumulating output.
 TAIL_CASES = [("fwd", (4096, 1024, 5120)), ("fwd", (5120, 1024, 4096)), ("bwd_data", (4096, 5120, 1024)),
-              ("bwd_weight", (1024, 4096, 5120)), ("bwd_weight", (1024, 5120, 4096))]
+              ("bwd_weight", (1024, 4096, 5120)), ("bwd_weight", (1024, 5120, 4096)),
+              ("fwd", (4096, 1000, 5120)), ("bwd_weight", (1000, 5120, 4096))]
 
 
 @pytest.mark.parametrize("op,shape", TAIL_CASES, ids=[f"{o}-{'x'.join(map(str, s))}" for o, s in TAIL_CASES])
@@ -473,16 +483,19 @@ def test_full_size_sampled(workload, gemm, orders):
                     f"copy={desc['copy']} pad={desc['pad']}")
             _check_sampled(c, op, what, rng)
         if g.N % 64:
-            # backward-data reduces over N, here not a multiple of 64: also force a
-            # plan that pads it, whatever the tuner picked
-            pid = next((p for p in range(F.fc_plan_count())
-                        if F.fc_set_plan(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16, p) == F.FC_OK
-                        and F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)["pad"] > 0),
-                       None)
-            assert pid is not None, "no padded plan applies"
-            desc = F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)
-            _check_sampled(c, "bwd_data", f"w{workload}g{gemm} bwd_data forced plan={pid} {desc['kernel']} "
-                                          f"pad={desc['pad']}", rng)
+            # backward-data reduces over N, here not a multiple of 64: also force
+            # both ring plans (three A tiles and three B tiles), which run the
+            # partial last stage themselves, whatever the tuner picked
+            forced = 0
+            for pid in (RING, RING_B):
+                if F.fc_set_plan(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16, pid) != F.FC_OK:
+                    continue
+                desc = F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)
+                assert desc["ktail"] == g.N % 64 and desc["pad"] == 0 and desc["ws"] == 0, desc
+                _check_sampled(c, "bwd_data", f"w{workload}g{gemm} bwd_data forced plan={pid} {desc['kernel']} "
+                                              f"ktail={desc['ktail']}", rng)
+                forced += 1
+            assert forced == 2, "a ring plan does not apply"
         del c
         torch.cuda.empty_cache()
 

@@ -46,8 +46,8 @@ def _clean_plans():
 
 
 # (M, K, N): reductions of 128 stages (head 2), 64 (head 4), 7 (padded form),
-# 1000 values (a padded reduction: 16 stages after the zero padding, head 4)
-# and ragged outputs
+# 1000 values (15 whole stages and a partial one, in front of two virtual
+# stages: padded form) and ragged outputs
 SHAPES = [(512, 8192, 768), (768, 4096, 512), (520, 448, 264), (256, 1000, 264)]
 
 
@@ -105,10 +105,14 @@ def test_stamped_products_are_the_hot_calls(shape, plan):
             for a, b in ((0, 2), (2, 3), (3, 4), (4, 5)):
                 assert np.all(s[:, b] >= s[:, a]), f"{what}: slot {b} before slot {a}"
             assert np.all(s[:, 6] > s[:, 1]), f"{what}: no wall time"
-            stages = -(-red // 64)
             assert desc["kernel"].endswith(", 3>" if plan == RING else ", 2>"), what
             padded = ", -1, " in desc["kernel"]
-            want_stages = stages + ((6 - stages % 6) % 6 if padded else 0)
+            whole = red // 64
+            if red % 64:  # the partial stage and the virtual ones in front of the whole stages
+                assert padded and desc["ktail"] == red % 64, what
+                want_stages = whole + 6 - whole % 6
+            else:
+                want_stages = whole + ((6 - whole % 6) % 6 if padded else 0)
             assert np.all(s[:, 7] == want_stages), f"{what}: stages {set(s[:, 7].tolist())} vs {want_stages}"
             r = F.summarize_stamps(s, wall_mhz)
             log(f"  clock {r['clock_GHz']:.3f} GHz, loop {r['loop_cycles_per_stage']:.0f} cycles/stage, "
