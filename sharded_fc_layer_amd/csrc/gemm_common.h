@@ -326,14 +326,34 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
             *reinterpret_cast<bf16x4*>(stage + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         }
     }
+    // Lane: 16-byte chunk ch of rows 4 q + rq. The reads go in groups of 16
+    // ahead of their stores, so their latencies overlap (one read, its wait
+    // and its store at a time cost about as much as the rest of the
+    // epilogue), and a wave tile wholly inside the output stores without
+    // per-row checks.
     const int rq = lane >> 4, ch = lane & 15;
+    const int64_t row0 = m0 + wm0 + rq, col = n0 + wn0 + ch * 8;
+    __bf16* c0 = static_cast<__bf16*>(g.C) + row0 * g.ldc + col;
+    const int64_t step = 4 * g.ldc;
+    const bool full = m0 + wm0 + 128 <= g.M && n0 + wn0 + 16 * TN <= g.N;
+    const bool col_in = col < g.N && (TN == 8 || ch < 2 * TN);
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-        const int row = q * 4 + rq;
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
-        const int64_t m = m0 + wm0 + row, n = n0 + wn0 + ch * 8;
-        if (m < g.M && n < g.N && (TN == 8 || ch < 2 * TN))
-            *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(g.C) + m * g.ldc + n) = v;
+    for (int qb = 0; qb < 32; qb += 16) {
+        bf16x8 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int row = (qb + u) * 4 + rq;
+            v[u] = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
+        }
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (TN == 8 || ch < 2 * TN) *reinterpret_cast<bf16x8*>(c0 + (qb + u) * step) = v[u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (col_in && row0 + 4 * (qb + u) < g.M) *reinterpret_cast<bf16x8*>(c0 + (qb + u) * step) = v[u];
+        }
     }
 }
 
@@ -375,14 +395,32 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
                 *reinterpret_cast<f32x4*>(stage + row * 512 + ((c4 ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
             }
         }
+        // reads in groups of 16 ahead of their stores, and no per-row checks
+        // for a half tile wholly inside the output (as in the bf16 epilogue)
+        const int64_t row0 = m0 + wm0 + 64 * h + rq, col = n0 + wn0 + 4 * ch;
+        float* c0 = C + row0 * g.ldc + col;
+        const int64_t step = 2 * g.ldc;
+        const bool full = m0 + wm0 + 64 * h + 64 <= g.M && n0 + wn0 + 16 * TN <= g.N;
+        const bool col_in = col < g.N && (TN == 8 || ch < 4 * TN);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int row = 2 * q + rq;
-            f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
-            const int64_t m = m0 + wm0 + 64 * h + row, n = n0 + wn0 + 4 * ch;
-            if (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN)) {
-                if (g.accumulate) v += old[q];
-                *reinterpret_cast<f32x4*>(C + m * g.ldc + n) = v;
+        for (int qb = 0; qb < 32; qb += 16) {
+            f32x4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int row = 2 * (qb + u) + rq;
+                v[u] = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (g.accumulate) v[u] += old[qb + u];
+            if (full) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (TN == 8 || ch < 4 * TN) *reinterpret_cast<f32x4*>(c0 + (qb + u) * step) = v[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (col_in && row0 + 2 * (qb + u) < g.M) *reinterpret_cast<f32x4*>(c0 + (qb + u) * step) = v[u];
             }
         }
     }
