@@ -105,6 +105,27 @@ __device__ constexpr int w64_load_spread(int nl, int u) {
     return (l < nl && (16 * l) / nl == g) ? l : -1;
 }
 
+// Zeroes the accumulators with MFMAs of zero operands (the MFMA pipe is
+// idle while the first stages load): written in place by asm outputs, the
+// zeros need no AGPR moves into the registers the asm MFMAs use (zeroed in
+// C++, they were materialised elsewhere, then copied, about 1000 cycles
+// after the first stage had landed). The zero operand is written by VALU
+// moves the compiler places just before: an MFMA reading a VGPR that a VALU
+// instruction wrote needs wait states first, which the compiler does not
+// insert ahead of asm, so each MFMA brings its own. w4_acc_fence (or, with
+// no stage to run, w4_acc_drain) must follow.
+template <int TN>
+__device__ __forceinline__ void w4_acc_zero(f32x4 (&acc)[8][TN]) {
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc[i][j]) : "v"(z));
+}
+
 // Orders every compiler write of the accumulators (their zero
 // initialisation, copies where control paths merge) before the asm MFMAs
 // that read them: every accumulator passes through an empty asm (so such

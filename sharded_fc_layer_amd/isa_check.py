@@ -14,7 +14,10 @@ tools and scans every kernel, in program order, for:
    ``READ_WINDOW`` slots, unless an ``s_waitcnt`` on ``vmcnt`` in between
    stalls the wave: at the places the kernels do this (after their main
    loops), that wait covers loads issued during the last MFMAs, which take
-   hundreds of cycles.
+   hundreds of cycles;
+3. a VALU write of a VGPR followed within ``VALU_WINDOW`` slots by an MFMA
+   that reads it as an operand (the accumulator zeroing builds its zero
+   operand with VALU moves right before its asm MFMAs).
 
 ``s_nop N`` counts N + 1 slots. The scan follows fall-through order only,
 and covers the kernels whose MFMAs are inline asm (``ASM_KERNELS``); the
@@ -36,6 +39,7 @@ TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 WRITE_WINDOW = 6   # slots between an AGPR write and an MFMA reading it
 READ_WINDOW = 18   # slots between an MFMA and a non-MFMA access of its result
+VALU_WINDOW = 2    # slots between a VALU write of a VGPR and an MFMA reading it
 ASM_KERNELS = re.compile(r"gemm_w4k64r?(_stamped)?_kernel")
 
 
@@ -81,24 +85,34 @@ def _agprs(tok: str) -> set:
     return {int(m.group(1))} if m else set()
 
 
+def _vgprs(tok: str) -> set:
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
 def scan(text: str) -> Dict[str, dict]:
     """Per kernel: MFMA count and the hazards found (list of strings)."""
     res: Dict[str, dict] = {}
     name = None
     wr: list = []   # (agprs, slots since a non-MFMA write)
     mw: list = []   # (agprs, slots since an MFMA wrote them)
+    vw: list = []   # (vgprs, slots since a VALU write)
 
     def age(n):
-        nonlocal wr, mw
+        nonlocal wr, mw, vw
         wr = [(r, s + n) for r, s in wr if s + n < WRITE_WINDOW]
         mw = [(r, s + n) for r, s in mw if s + n < READ_WINDOW]
+        vw = [(r, s + n) for r, s in vw if s + n < VALU_WINDOW]
 
     for line in text.split("\n"):
         m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
         if m:
             name = m.group(1)
             res[name] = {"mfma": 0, "hazards": []}
-            wr, mw = [], []
+            wr, mw, vw = [], [], []
             continue
         if name is None:
             continue
@@ -120,6 +134,10 @@ def scan(text: str) -> Dict[str, dict]:
             for r, s in wr:
                 if r & srcc:
                     res[name]["hazards"].append(f"MFMA reads a{min(r & srcc)} {s} slots after a write: {t}")
+            srcv = set().union(*[_vgprs(o) for o in ops[1:4]]) if len(ops) > 1 else set()
+            for r, s in vw:
+                if r & srcv:
+                    res[name]["hazards"].append(f"MFMA reads v{min(r & srcv)} {s} slots after a VALU write: {t}")
             age(1)
             dst = _agprs(ops[0]) if ops else set()
             if dst:
@@ -134,6 +152,9 @@ def scan(text: str) -> Dict[str, dict]:
             dst = _agprs(ops[0]) if ops else set()
             if dst:
                 wr.append((dst, 0))
+            vdst = _vgprs(ops[0]) if ops else set()
+            if vdst:
+                vw.append((vdst, 0))
             continue
         age(1)
     return res

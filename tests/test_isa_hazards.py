@@ -53,6 +53,22 @@ def test_write_right_before_an_mfma_is_found():
     assert not _hazards(text_ok)
 
 
+def test_valu_write_of_an_mfma_operand_is_found():
+    """The form a real fault took: the zero operand of the accumulator-zeroing
+    MFMAs moved into place by VALU instructions right before them, so the
+    first MFMA read stale values and left garbage in an accumulator."""
+    text = HEAD + "\tv_mov_b64_e32 v[4:5], s[30:31]\n" + \
+        "\tv_mfma_f32_16x16x32_bf16 a[252:255], v[2:5], v[2:5], 0\n"
+    h = _hazards(text)
+    assert len(h) == 1 and "v4" in h[0] and "VALU" in h[0]
+    assert _hazards(HEAD + "\tv_mov_b32_e32 v3, 0\n\ts_nop 0\n"
+                    "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[2:5], v[2:5], 0\n")  # 1 slot: too few
+    assert not _hazards(HEAD + "\tv_mov_b32_e32 v3, 0\n\ts_nop 1\n"
+                        "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[2:5], v[2:5], 0\n")
+    assert not _hazards(HEAD + "\tv_mov_b32_e32 v9, 0\n"
+                        "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[2:5], v[2:5], 0\n")  # another register
+
+
 LIB = os.path.join(os.path.dirname(C.HERE), "sharded_fc_layer_amd", "libfcshard.so")
 
 
