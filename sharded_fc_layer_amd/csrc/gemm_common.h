@@ -141,22 +141,26 @@ struct DmaPP {
     uint32_t base[kInstr];
     int kk[kInstr];
 
+    // 32-bit unsigned arithmetic: the operand is smaller than 2 GiB, so every
+    // in-range offset fits, and rows and row0 are below 2^32 (an offset of a
+    // row past the operand may wrap: it is replaced by kOOB)
     __device__ __forceinline__ void init(int wq, int lane, int64_t ld, int64_t row0, int64_t rows) {
+        const uint32_t ld32 = (uint32_t)ld, r0 = (uint32_t)row0, nrows = (uint32_t)rows;
 #pragma unroll
         for (int j = 0; j < kInstr; ++j) {
-            const int p = (wq * kInstr + j) * 64 + lane;  // 16-byte slot in the tile
+            const uint32_t p = (uint32_t)((wq * kInstr + j) * 64 + lane);  // 16-byte slot in the tile
             if (!OC) {
-                constexpr int CPR = BKP / 8;
-                const int i = p / CPR, pc = p % CPR;
-                const int c = pc ^ rc_swizzle<BKP>(i);
-                kk[j] = 8 * c;
-                base[j] = (row0 + i < rows) ? (uint32_t)(((row0 + i) * ld + 8 * c) * 2) : kOOB;
+                constexpr uint32_t CPR = BKP / 8;
+                const uint32_t i = p / CPR, pc = p % CPR;
+                const uint32_t c = pc ^ (uint32_t)rc_swizzle<BKP>((int)i);
+                kk[j] = (int)(8 * c);
+                base[j] = r0 + i < nrows ? ((r0 + i) * ld32 + 8 * c) * 2 : kOOB;
             } else {
-                constexpr int CPR = R / 8;
-                const int k = p / CPR;
-                const int c = (p % CPR) ^ oc_swizzle_r<R>(k);
-                kk[j] = k;
-                base[j] = (row0 + 8 * c < rows) ? (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2) : kOOB;
+                constexpr uint32_t CPR = R / 8;
+                const uint32_t k = p / CPR;
+                const uint32_t c = (p % CPR) ^ (uint32_t)oc_swizzle_r<R>((int)k);
+                kk[j] = (int)k;
+                base[j] = r0 + 8 * c < nrows ? (k * ld32 + r0 + 8 * c) * 2 : kOOB;
             }
         }
     }
