@@ -155,9 +155,10 @@ int64_t fc_noalloc_scratch_bytes(void);
  * exhaustive search (else quick); bit 1: time with warm caches. By default
  * every timed launch follows a 512 MB copy that evicts the L2s and the MALL,
  * so plans are ranked on operands read from HBM, as in a training step
- * (warm caches are used if those buffers cannot be allocated). Allocates
- * temporary buffers and may grow the workspace; synchronizes `stream`.
- * Plans are kept until fc_release.
+ * (warm caches are used if those buffers cannot be allocated). Candidates
+ * within 3 % of the fastest (at most four) are timed again in interleaved
+ * rounds before the pick. Allocates temporary buffers and may grow the
+ * workspace; synchronizes `stream`. Plans are kept until fc_release.
  */
 fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_order,
                   fc_out_dtype out_dtype, int flags, void* stream);
@@ -177,9 +178,13 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
 /*
  * Describes the plan a hot call at this key would run: writes a NUL-terminated
  * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> pad=<k>
- * ws=<bytes>" into buf (truncated to len); pad is the length the reduction
- * is zero-padded to (reduction-contiguous operands copied into the
- * workspace), 0 for none. It is followed by " tuned_ms=<t>" when fc_tune chose
+ * ktail=<t> ws=<bytes>" into buf (truncated to len); pad is the length the
+ * reduction is zero-padded to (reduction-contiguous operands copied into the
+ * workspace), 0 for none; ktail is, for the ring kernels, the number of
+ * reduction values past the last whole 64-value stage (the partial stage they
+ * load themselves), else 0. A tail-split plan adds " tail=n<cols>" or
+ * " tail=m<rows>", the extent of its unsplit part. The text is followed by
+ * " tuned_ms=<t>" when fc_tune chose
  * the plan (or a loaded plan file recorded its time): the median time of one
  * launch, in ms, as fc_tune measured it. Returns FC_E_INVALID for bad
  * arguments.

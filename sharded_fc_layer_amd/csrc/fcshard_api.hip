@@ -741,7 +741,7 @@ struct CacheFlush {
 // Median of `reps` single-launch times after `warm` untimed launches; with
 // `flush`, the caches are flushed before every timed launch.
 float time_plan(const Problem& p, const Plan& pl, void* ws, hipStream_t s, int warm, int reps, hipEvent_t* ev,
-                const CacheFlush* flush, bool* ok) {
+                const CacheFlush* flush, bool* ok, std::vector<float>* samples = nullptr) {
     *ok = true;
     for (int i = 0; i < warm; ++i)
         if (run_plan(p, pl, ws, s) != hipSuccess) *ok = false;
@@ -757,8 +757,14 @@ float time_plan(const Problem& p, const Plan& pl, void* ws, hipStream_t s, int w
         t.push_back(ms);
     }
     if (!*ok || t.empty()) return 1e30f;
+    if (samples) samples->insert(samples->end(), t.begin(), t.end());
     std::sort(t.begin(), t.end());
     return t[t.size() / 2];
+}
+
+float median_of(std::vector<float> v) {
+    std::sort(v.begin(), v.end());
+    return v[v.size() / 2];
 }
 
 }  // namespace
@@ -977,15 +983,45 @@ fc_status fc_tune(int64_t M, int64_t K, int64_t N, fc_order x_order, fc_order w_
         int best = -1;
         float best_ms = 1e30f;
         std::vector<std::pair<int, float>> times;
+        std::vector<std::vector<float>> samples;  // per entry of times
         for (int id : cand) {
             bool ok;
-            const float ms = time_plan(p, decode_plan(id), ws, s, warm, reps, ev, flush, &ok);
+            std::vector<float> t;
+            const float ms = time_plan(p, decode_plan(id), ws, s, warm, reps, ev, flush, &ok, &t);
             if (!ok) {
                 (void)hipGetLastError();
                 continue;
             }
             times.push_back({id, ms});
+            samples.push_back(t);
             if (ms < best_ms) best_ms = ms, best = id;
+        }
+        // The close candidates (within 3 % of the best, at most four) are timed
+        // again in interleaved rounds and each keeps the median of all its
+        // samples: five timed launches leave 2-4 % of noise, enough to flip a
+        // pick, and the rounds spread any drift of the clock over all of them.
+        {
+            std::vector<size_t> close;
+            for (size_t c = 0; c < times.size(); ++c)
+                if (times[c].second <= best_ms * 1.03f) close.push_back(c);
+            std::sort(close.begin(), close.end(),
+                      [&](size_t a, size_t b) { return times[a].second < times[b].second; });
+            if (close.size() > 4) close.resize(4);
+            if (close.size() > 1) {
+                constexpr int kRounds = 4, kRoundReps = 3;
+                for (int r = 0; r < kRounds; ++r)
+                    for (size_t c : close) {
+                        bool ok;
+                        time_plan(p, decode_plan(times[c].first), ws, s, 1, kRoundReps, ev, flush, &ok, &samples[c]);
+                        if (!ok) (void)hipGetLastError();
+                    }
+                best_ms = 1e30f;
+                for (size_t c = 0; c < times.size(); ++c) {
+                    if (std::find(close.begin(), close.end(), c) != close.end())
+                        times[c].second = median_of(samples[c]);
+                    if (times[c].second < best_ms) best_ms = times[c].second, best = times[c].first;
+                }
+            }
         }
         // tie-break within 1%: no workspace, then no split, then the lower id
         int pick = best;
