@@ -261,6 +261,33 @@ def test_exact_tail_split_plans(op, shape):
     assert ran >= 8
 
 
+def test_ring_partial_stage_needs_a_whole_stage_before_it():
+    """A ring kernel runs a reduction's partial last stage only after at least
+    one whole 64-value stage (its trailing prefetches reload the last whole
+    one): forward reductions of 8 and 40 values refuse the ring plans, one of
+    72 (a whole stage and 8 values) runs them exactly, with no workspace."""
+    M, N = 264, 136
+    for K, applies in ((8, False), (40, False), (72, True)):
+        d = I.make_integer_inputs(M, K, N, seed=K)
+        c = Case(d, ROW, ROW)
+        O, _ = c.oracle("fwd")
+        for pid in (RING, RING_B):
+            st = F.fc_set_plan(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16, pid)
+            if not applies:
+                assert st == F.FC_E_UNSUPPORTED, (K, pid, F.status_str(st))
+                continue
+            assert st == F.FC_OK, (K, pid, F.status_str(st))
+            desc = F.fc_plan_describe(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16)
+            assert desc["ktail"] == K % 64 and desc["ws"] == 0 and desc["pad"] == 0, desc
+            what = f"fwd {(M, K, N)} plan={pid} {desc['kernel']}"
+            log(what)
+            G = host(c.gpu("fwd", F.OUT_BF16))
+            torch.cuda.synchronize()
+            assert_exact(G, O, F.OUT_BF16, what)
+        F.fc_set_plan(F.OP_FWD, M, K, N, ROW, ROW, F.OUT_BF16, -1)
+        del c
+
+
 def test_default_plans_need_no_workspace():
     """Untuned shapes run a plan that needs no workspace, also where the
     one-wave-per-SIMD kernels could only run the reduction padded (K = 2040 is
