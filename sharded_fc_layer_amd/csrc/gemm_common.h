@@ -319,45 +319,52 @@ template <int TN>
 __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_t m0, int64_t n0, int wm0, int wn0,
                                                        int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = i * 16 + lr;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = j * 16 + lk * 4;
-            const uint32_t off = row * 256 + (((col >> 3) ^ (row & 15)) << 4) + ((col & 7) << 1);
-            const f32x4 v = acc[i][j];
-            *reinterpret_cast<bf16x4*>(stage + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        }
-    }
-    // Lane: 16-byte chunk ch of rows 4 q + rq. The reads go in groups of 16
-    // ahead of their stores, so their latencies overlap (one read, its wait
-    // and its store at a time cost about as much as the rest of the
-    // epilogue), and a wave tile wholly inside the output stores without
-    // per-row checks.
+    // Reading back: lane = 16-byte chunk ch of rows 4 u + rq of a 16-row
+    // group. A wave tile wholly inside the output stores without per-row checks.
     const int rq = lane >> 4, ch = lane & 15;
     const int64_t row0 = m0 + wm0 + rq, col = n0 + wn0 + ch * 8;
     __bf16* c0 = static_cast<__bf16*>(g.C) + row0 * g.ldc + col;
     const int64_t step = 4 * g.ldc;
     const bool full = m0 + wm0 + 128 <= g.M && n0 + wn0 + 16 * TN <= g.N;
     const bool col_in = col < g.N && (TN == 8 || ch < 2 * TN);
+    // Software-pipelined over the 8 groups of 16 rows (acc[i]): group i is
+    // converted and written while group i - 1's 4 stores drain, then read
+    // back, so the AGPR reads and conversions (VALU) overlap the stores
+    // (texture path) instead of preceding them all.
+    bf16x8 v[2][4];
 #pragma unroll
-    for (int qb = 0; qb < 32; qb += 16) {
-        bf16x8 v[16];
+    for (int i = 0; i <= 8; ++i) {
+        if (i < 8) {  // convert and write group i
+            const int row = i * 16 + lr;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int row = (qb + u) * 4 + rq;
-            v[u] = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
+            for (int j = 0; j < TN; ++j) {
+                const int cc = j * 16 + lk * 4;
+                const uint32_t off = row * 256 + (((cc >> 3) ^ (row & 15)) << 4) + ((cc & 7) << 1);
+                const f32x4 a = acc[i][j];
+                *reinterpret_cast<bf16x4*>(stage + off) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+            }
         }
-        if (full) {
+        if (i > 0) {  // store group i - 1 (rows 16 (i - 1) + 4 u + rq)
+            const bf16x8* w = v[(i - 1) & 1];
+            if (full) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (TN == 8 || ch < 2 * TN) *reinterpret_cast<bf16x8*>(c0 + (qb + u) * step) = v[u];
-        } else {
+                for (int u = 0; u < 4; ++u)
+                    if (TN == 8 || ch < 2 * TN) *reinterpret_cast<bf16x8*>(c0 + (4 * (i - 1) + u) * step) = w[u];
+            } else {
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (col_in && row0 + 4 * (qb + u) < g.M) *reinterpret_cast<bf16x8*>(c0 + (qb + u) * step) = v[u];
+                for (int u = 0; u < 4; ++u)
+                    if (col_in && row0 + 16 * (i - 1) + 4 * u < g.M)
+                        *reinterpret_cast<bf16x8*>(c0 + (4 * (i - 1) + u) * step) = w[u];
+            }
         }
+        if (i < 8) {  // read group i back
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = i * 16 + 4 * u + rq;
+                v[i & 1][u] = *reinterpret_cast<const bf16x8*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
+            }
+        }
+        asm volatile("" ::: "memory");  // keeps the groups in this order
     }
 }
 
