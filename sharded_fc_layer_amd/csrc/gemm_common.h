@@ -369,72 +369,73 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
 }
 
 // fp32 epilogue of the same wave tile (fp32 and accumulating outputs,
-// split-K partial planes), staged the same way in two passes of 64 rows:
-// LDS rows of 512 B with the 16-byte chunk XOR-swizzled by (row & 7) << 1,
-// which spreads both a half-wave's writes and a row's reads evenly over the
-// banks. Each store writes 2 rows x 512 B of whole lines; an accumulating
-// output is read back the same way and added. Within one wave, LDS accesses
-// complete in order, so the second pass may overwrite what the first read.
+// split-K partial planes), staged the same way and software-pipelined over
+// the eight 16-row groups like the bf16 one: group i is written into one of
+// two 8 KB LDS buffers (rows of 512 B, the 16-byte chunk XOR-swizzled by
+// (row & 7) << 1, which spreads both a half-wave's writes and a row's reads
+// evenly over the banks) while group i - 1's stores drain, then read back.
+// Each store writes 2 rows x 512 B of whole lines. An accumulating output's
+// old values are loaded one group ahead, so their latency overlaps a group's
+// work, and added before the store. Within one wave, LDS accesses complete
+// in order, so group i + 2 may overwrite the buffer group i was read from.
 template <int TN>
 __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int slice, int64_t m0, int64_t n0, int wm0,
                                                       int wn0, int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
     float* C = static_cast<float*>(g.C) + (int64_t)slice * g.c_split_stride;
+    // reading back: lane = 16-byte chunk ch of rows 2 u + rq of a group
     const int rq = lane >> 5, ch = lane & 31;
+    const int64_t row0 = m0 + wm0 + rq, col = n0 + wn0 + 4 * ch;
+    float* c0 = C + row0 * g.ldc + col;
+    const int64_t step = 2 * g.ldc;
+    const bool full = m0 + wm0 + 128 <= g.M && n0 + wn0 + 16 * TN <= g.N;
+    const bool col_in = col < g.N && (TN == 8 || ch < 4 * TN);
+    f32x4 v[2][8], old[2][8];
+    // the old values of group gi (accumulating output), zeros outside the output
+#define FC_F32_LOAD_OLD(GI)                                                                                \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                                        \
+        const int r_ = 16 * (GI) + 2 * u;                                                                  \
+        old[(GI) & 1][u] = (col_in && row0 + r_ < g.M) ? *reinterpret_cast<const f32x4*>(c0 + (8 * (GI) + u) * step) \
+                                                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};                     \
+    }
+    if (g.accumulate) FC_F32_LOAD_OLD(0)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        // an accumulating output: all of this half's old values are loaded
-        // first, so their latencies overlap (loaded one by one between the
-        // stores, each load waited out on its own: the compiler cannot prove
-        // that they do not alias the stores before them)
-        f32x4 old[32];
-        if (g.accumulate) {
-#pragma unroll
-            for (int q = 0; q < 32; ++q) {
-                const int64_t m = m0 + wm0 + 64 * h + 2 * q + rq, n = n0 + wn0 + 4 * ch;
-                old[q] = (m < g.M && n < g.N && (TN == 8 || ch < 4 * TN))
-                             ? *reinterpret_cast<const f32x4*>(C + m * g.ldc + n)
-                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = i * 16 + lr;
+    for (int i = 0; i <= 8; ++i) {
+        if (i < 8) {  // write group i
+            char* buf = stage + (i & 1) * 8192;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int c4 = 4 * j + lk;
-                *reinterpret_cast<f32x4*>(stage + row * 512 + ((c4 ^ ((row & 7) << 1)) << 4)) = acc[4 * h + i][j];
+                *reinterpret_cast<f32x4*>(buf + lr * 512 + ((c4 ^ ((lr & 7) << 1)) << 4)) = acc[i][j];
             }
         }
-        // reads in groups of 16 ahead of their stores, and no per-row checks
-        // for a half tile wholly inside the output (as in the bf16 epilogue)
-        const int64_t row0 = m0 + wm0 + 64 * h + rq, col = n0 + wn0 + 4 * ch;
-        float* c0 = C + row0 * g.ldc + col;
-        const int64_t step = 2 * g.ldc;
-        const bool full = m0 + wm0 + 64 * h + 64 <= g.M && n0 + wn0 + 16 * TN <= g.N;
-        const bool col_in = col < g.N && (TN == 8 || ch < 4 * TN);
+        if (i > 0) {  // store group i - 1 (rows 16 (i - 1) + 2 u + rq)
+            const int gi = i - 1;
+            f32x4 w[8];
 #pragma unroll
-        for (int qb = 0; qb < 32; qb += 16) {
-            f32x4 v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int row = 2 * (qb + u) + rq;
-                v[u] = *reinterpret_cast<const f32x4*>(stage + row * 512 + ((ch ^ ((row & 7) << 1)) << 4));
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (g.accumulate) v[u] += old[qb + u];
+            for (int u = 0; u < 8; ++u) w[u] = g.accumulate ? v[gi & 1][u] + old[gi & 1][u] : v[gi & 1][u];
             if (full) {
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (TN == 8 || ch < 4 * TN) *reinterpret_cast<f32x4*>(c0 + (qb + u) * step) = v[u];
+                for (int u = 0; u < 8; ++u)
+                    if (TN == 8 || ch < 4 * TN) *reinterpret_cast<f32x4*>(c0 + (8 * gi + u) * step) = w[u];
             } else {
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (col_in && row0 + 2 * (qb + u) < g.M) *reinterpret_cast<f32x4*>(c0 + (qb + u) * step) = v[u];
+                for (int u = 0; u < 8; ++u)
+                    if (col_in && row0 + 16 * gi + 2 * u < g.M) *reinterpret_cast<f32x4*>(c0 + (8 * gi + u) * step) = w[u];
             }
         }
+        if (i < 8) {
+            if (i + 1 < 8 && g.accumulate) FC_F32_LOAD_OLD(i + 1)
+            const char* buf = stage + (i & 1) * 8192;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = 2 * u + rq;
+                v[i & 1][u] = *reinterpret_cast<const f32x4*>(buf + r * 512 + ((ch ^ ((r & 7) << 1)) << 4));
+            }
+        }
+        asm volatile("" ::: "memory");  // keeps the groups in this order
     }
+#undef FC_F32_LOAD_OLD
 }
 
 // Output tile and reduction slice of this block. Blocks are dealt round robin
