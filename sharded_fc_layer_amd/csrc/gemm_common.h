@@ -320,10 +320,12 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
                                                        int lane, const f32x4 (&acc)[8][TN], char* stage) {
     const int lr = lane & 15, lk = lane >> 4;
     // Reading back: lane = 16-byte chunk ch of rows 4 u + rq of a 16-row
-    // group. A wave tile wholly inside the output stores without per-row checks.
+    // group. Rows are stored in order, so the store address is one running
+    // pointer (an add per store); a wave tile wholly inside the output
+    // stores without per-row checks.
     const int rq = lane >> 4, ch = lane & 15;
     const int64_t row0 = m0 + wm0 + rq, col = n0 + wn0 + ch * 8;
-    __bf16* c0 = static_cast<__bf16*>(g.C) + row0 * g.ldc + col;
+    __bf16* cp = static_cast<__bf16*>(g.C) + row0 * g.ldc + col;
     const int64_t step = 4 * g.ldc;
     const bool full = m0 + wm0 + 128 <= g.M && n0 + wn0 + 16 * TN <= g.N;
     const bool col_in = col < g.N && (TN == 8 || ch < 2 * TN);
@@ -349,13 +351,13 @@ __device__ __forceinline__ void store_tile_bf16_staged(const GemmArgs& g, int64_
             if (full) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (TN == 8 || ch < 2 * TN) *reinterpret_cast<bf16x8*>(c0 + (4 * (i - 1) + u) * step) = w[u];
+                    if (TN == 8 || ch < 2 * TN) *reinterpret_cast<bf16x8*>(cp + u * step) = w[u];
             } else {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (col_in && row0 + 16 * (i - 1) + 4 * u < g.M)
-                        *reinterpret_cast<bf16x8*>(c0 + (4 * (i - 1) + u) * step) = w[u];
+                    if (col_in && row0 + 16 * (i - 1) + 4 * u < g.M) *reinterpret_cast<bf16x8*>(cp + u * step) = w[u];
             }
+            cp += 4 * step;
         }
         if (i < 8) {  // read group i back
 #pragma unroll
