@@ -388,7 +388,10 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
     // reading back: lane = 16-byte chunk ch of rows 2 u + rq of a group
     const int rq = lane >> 5, ch = lane & 31;
     const int64_t row0 = m0 + wm0 + rq, col = n0 + wn0 + 4 * ch;
-    float* c0 = C + row0 * g.ldc + col;
+    // running pointers (an add per access): stores, and an accumulating
+    // output's old values one group ahead
+    float* cp = C + row0 * g.ldc + col;
+    const float* op = cp;
     const int64_t step = 2 * g.ldc;
     const bool full = m0 + wm0 + 128 <= g.M && n0 + wn0 + 16 * TN <= g.N;
     const bool col_in = col < g.N && (TN == 8 || ch < 4 * TN);
@@ -397,9 +400,10 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
 #define FC_F32_LOAD_OLD(GI)                                                                                \
     _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                                        \
         const int r_ = 16 * (GI) + 2 * u;                                                                  \
-        old[(GI) & 1][u] = (col_in && row0 + r_ < g.M) ? *reinterpret_cast<const f32x4*>(c0 + (8 * (GI) + u) * step) \
+        old[(GI) & 1][u] = (col_in && row0 + r_ < g.M) ? *reinterpret_cast<const f32x4*>(op + u * step)    \
                                                        : f32x4{0.0f, 0.0f, 0.0f, 0.0f};                     \
-    }
+    }                                                                                                      \
+    op += 8 * step;
     if (g.accumulate) FC_F32_LOAD_OLD(0)
 #pragma unroll
     for (int i = 0; i <= 8; ++i) {
@@ -419,12 +423,13 @@ __device__ __forceinline__ void store_tile_f32_staged(const GemmArgs& g, int sli
             if (full) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (TN == 8 || ch < 4 * TN) *reinterpret_cast<f32x4*>(c0 + (8 * gi + u) * step) = w[u];
+                    if (TN == 8 || ch < 4 * TN) *reinterpret_cast<f32x4*>(cp + u * step) = w[u];
             } else {
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (col_in && row0 + 16 * gi + 2 * u < g.M) *reinterpret_cast<f32x4*>(c0 + (8 * gi + u) * step) = w[u];
+                    if (col_in && row0 + 16 * gi + 2 * u < g.M) *reinterpret_cast<f32x4*>(cp + u * step) = w[u];
             }
+            cp += 8 * step;
         }
         if (i < 8) {
             if (i + 1 < 8 && g.accumulate) FC_F32_LOAD_OLD(i + 1)
