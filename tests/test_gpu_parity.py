@@ -261,6 +261,29 @@ def test_exact_tail_split_plans(op, shape):
     assert ran >= 8
 
 
+@pytest.mark.parametrize("exhaustive,warm", [(True, True), (False, False)], ids=["exhaustive-warm", "quick-flushed"])
+def test_tuned_plans_exact(exhaustive, warm):
+    """fc_tune in both candidate sets and both cache modes (its close
+    candidates re-timed in rounds) picks plans that are exact on integer data,
+    for every product and storage order, on ragged sizes."""
+    M, K, N = 520, 1032, 264
+    d = I.make_integer_inputs(M, K, N, seed=21)
+    for xo, wo in ALL_ORDERS:
+        c = Case(d, xo, wo)
+        F.fc_tune(M, K, N, xo, wo, F.OUT_BF16, exhaustive=exhaustive, warm_caches=warm)
+        for op in OPS:
+            desc = F.fc_plan_describe(op_code(op), M, K, N, xo, wo, F.OUT_BF16)
+            assert desc.get("tuned_ms", 0) > 0, desc
+            what = f"tuned {op} orders={xo}{wo} plan={desc['plan']} {desc['kernel']}"
+            log(what)
+            O, _ = c.oracle(op)
+            G = host(c.gpu(op, F.OUT_BF16))
+            torch.cuda.synchronize()
+            assert_exact(G, O, F.OUT_BF16, what)
+        del c
+    F.fc_release()
+
+
 def test_ring_partial_stage_needs_a_whole_stage_before_it():
     """A ring kernel runs a reduction's partial last stage only after at least
     one whole 64-value stage (its trailing prefetches reload the last whole
