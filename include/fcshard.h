@@ -178,9 +178,13 @@ fc_status fc_set_plan(fc_op op, int64_t M, int64_t K, int64_t N, fc_order x_orde
 /*
  * Describes the plan a hot call at this key would run: writes a NUL-terminated
  * text "plan=<id> kernel=<name> tile=<BMxBN> split=<s> copy=<mask> pad=<k>
- * ktail=<t> ws=<bytes>" into buf (truncated to len); pad is the length the
- * reduction is zero-padded to (reduction-contiguous operands copied into the
- * workspace), 0 for none; ktail is, for the ring kernels, the number of
+ * ktail=<t> ws=<bytes>" into buf (truncated to len); copy has bit 0 for the
+ * first operand (X or dY) and bit 1 for the second (W or dY), each a copy in
+ * the workspace: transposed if the operand is output-contiguous, else (ring
+ * kernels, a reduction that is not a multiple of 64) with rows padded to
+ * whole 64-value stages; pad is the length the reduction is zero-padded to
+ * (reduction-contiguous operands copied into the workspace), 0 for none;
+ * ktail is, for the ring kernels, the number of
  * reduction values past the last whole 64-value stage (the partial stage they
  * load themselves), else 0. A tail-split plan adds " tail=n<cols>" or
  * " tail=m<rows>", the extent of its unsplit part. The text is followed by
@@ -277,8 +281,9 @@ fc_status fc_mfma_probe_launch(int64_t iters, int blocks, void* clocks, void* st
  *
  * Only plans whose product is one ring-kernel launch have a stamped form:
  * family 8 or 9, 256-column tiles, one reduction slice, no tail split, no
- * transpose copy, bf16 output. A padded reduction is allowed. Any other plan returns
- * FC_E_UNSUPPORTED, and nothing is enqueued.
+ * operand copy (transposed or padded), bf16 output. A reduction that is not a
+ * multiple of 64 is allowed (the ring loads its partial stage). Any other plan
+ * returns FC_E_UNSUPPORTED, and nothing is enqueued.
  * FC_E_INVALID: a NULL, misaligned or too small stamps buffer, or arguments
  * the hot call would refuse.
  */

@@ -138,13 +138,26 @@ void split_geometry(int64_t K, int split, int64_t* k_split, int* slices) {
     *slices = (int)((K + ks - 1) / ks);
 }
 
-// Family 7 runs reductions that are not a multiple of 64 by padding: each
-// reduction-contiguous operand is copied to rows of round_up(K, 64) values
-// with zeros past K (its last 64-value stage then reads zeros there), while
-// output-contiguous operands read zeros past row K through their buffer
-// bounds. Plans with a transpose copy do not pad. The rings (families 8 and
-// 9) load such a partial stage themselves, chunks past K reading zeros.
-bool pads_reduction(const Problem& p, const Plan& pl) { return pl.family == kFamilyW4 + 1 && p.K % 64 != 0; }
+// A reduction that is not a multiple of 64 ends with a partial stage.
+// Family 7 pads it: each reduction-contiguous operand is copied to rows of
+// round_up(K, 64) values with zeros past K (its last 64-value stage then
+// reads zeros there), while output-contiguous operands read zeros past row K
+// through their buffer bounds. The rings (families 8 and 9) load the partial
+// stage themselves, chunks past K reading zeros, and copy a
+// reduction-contiguous operand to such padded rows only when the plan's copy
+// bit for it is set: rows of K values then start part-way into a 128-byte
+// line (every other row when K is an odd multiple of 32), so that a stage
+// of them touches two lines, which the copy trades for its own traffic (the
+// tuner weighs it). A plan does not combine padding with a transpose copy.
+bool pads_a(const Problem& p, const Plan& pl) {
+    if (p.K % 64 == 0 || p.a_oc) return false;
+    return pl.family == kFamilyW4 + 1 || (pl.family >= kFamilyW4 + 2 && (pl.copy & 1));
+}
+bool pads_b(const Problem& p, const Plan& pl) {
+    if (p.K % 64 == 0 || p.b_oc) return false;
+    return pl.family == kFamilyW4 + 1 || (pl.family >= kFamilyW4 + 2 && (pl.copy & 2));
+}
+bool pads_reduction(const Problem& p, const Plan& pl) { return pads_a(p, pl) || pads_b(p, pl); }
 
 struct WsLayout {
     int64_t a_off, b_off, p_off, total;
@@ -153,15 +166,15 @@ struct WsLayout {
 WsLayout ws_layout(const Problem& p, const Plan& pl) {
     WsLayout w{0, 0, 0, 0};
     int64_t off = 0;
-    const bool pad = pads_reduction(p, pl);
+    const bool pad_a = pads_a(p, pl), pad_b = pads_b(p, pl);
     const int64_t kp = round_up(p.K, 64);
-    if (((pl.copy & 1) && p.a_oc) || (pad && !p.a_oc)) {
+    if (((pl.copy & 1) && p.a_oc) || pad_a) {
         w.a_off = off;
-        off += round_up(p.M * (pad ? kp : p.K) * 2, 256);
+        off += round_up(p.M * (pad_a ? kp : p.K) * 2, 256);
     }
-    if (((pl.copy & 2) && p.b_oc) || (pad && !p.b_oc)) {
+    if (((pl.copy & 2) && p.b_oc) || pad_b) {
         w.b_off = off;
-        off += round_up(p.N * (pad ? kp : p.K) * 2, 256);
+        off += round_up(p.N * (pad_b ? kp : p.K) * 2, 256);
     }
     int64_t ks;
     int slices;
@@ -181,8 +194,11 @@ WsLayout ws_layout(const Problem& p, const Plan& pl) {
 
 // Is the plan meaningful for this problem?
 bool plan_applies(const Problem& p, const Plan& pl) {
-    if ((pl.copy & 1) && !p.a_oc) return false;
-    if ((pl.copy & 2) && !p.b_oc) return false;
+    // a copy bit transposes an output-contiguous operand, or (rings, a
+    // reduction that is not a multiple of 64) pads a reduction-contiguous one
+    const bool ring_pads = pl.family >= kFamilyW4 + 2 && p.K % 64 != 0;
+    if ((pl.copy & 1) && !p.a_oc && !ring_pads) return false;
+    if ((pl.copy & 2) && !p.b_oc && !ring_pads) return false;
     const bool aligned_after_copy = p.M % 8 == 0 && p.N % 8 == 0 && p.K % 8 == 0 &&
                                     (uintptr_t)p.C % 16 == 0 &&
                                     ((pl.copy & 1) || (uintptr_t)p.A % 16 == 0) &&
@@ -200,7 +216,12 @@ bool plan_applies(const Problem& p, const Plan& pl) {
             const int64_t last = (p.K - (int64_t)(slices - 1) * ks + 63) / 64;
             if (first % 2 != 0 || last % 2 != 0) return false;
         }
-        if (pads_reduction(p, pl) && pl.copy != 0) return false;
+        // family 7 pads every reduction-contiguous operand itself, a
+        // transposed copy included, so it takes no copy then; a ring does not
+        // combine a padded copy with a transposed one
+        if (pl.family == kFamilyW4 + 1 && p.K % 64 != 0 && pl.copy != 0) return false;
+        const bool transposes = ((pl.copy & 1) && p.a_oc) || ((pl.copy & 2) && p.b_oc);
+        if (pads_reduction(p, pl) && transposes) return false;
         // a ring runs a partial last stage after at least one whole one (in
         // the slice that ends the reduction; a tail plan's main launch is
         // unsplit)
@@ -208,8 +229,8 @@ bool plan_applies(const Problem& p, const Plan& pl) {
             return false;
     }
     if (pl.family != 1) {
-        const int64_t k_a = pads_reduction(p, pl) && !p.a_oc ? round_up(p.K, 64) : p.K;
-        const int64_t k_b = pads_reduction(p, pl) && !p.b_oc ? round_up(p.K, 64) : p.K;
+        const int64_t k_a = pads_a(p, pl) ? round_up(p.K, 64) : p.K;
+        const int64_t k_b = pads_b(p, pl) ? round_up(p.K, 64) : p.K;
         const int64_t a_bytes = ((pl.copy & 1) ? 0 : p.M * k_a * 2);
         const int64_t b_bytes = ((pl.copy & 2) ? 0 : p.N * k_b * 2);
         if (a_bytes >= kPipeMaxBytes || b_bytes >= kPipeMaxBytes || p.M * p.K * 2 >= kPipeMaxBytes ||
@@ -363,13 +384,13 @@ hipError_t run_plan(const Problem& p0, const Plan& pl, void* ws, hipStream_t s,
     }
     if (pads_reduction(p0, pl)) {  // reduction-contiguous operands to rows of round_up(K, 64), zeros past K
         const int64_t kp = round_up(p.K, 64);
-        if (!p.a_oc) {
+        if (pads_a(p0, pl)) {
             uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.a_off);
             if ((e = launch_pad_rows_bf16(p.A, dst, p.M, p.K, kp, s)) != hipSuccess) return e;
             p.A = dst;
             lda = kp;
         }
-        if (!p.b_oc) {
+        if (pads_b(p0, pl)) {
             uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.b_off);
             if ((e = launch_pad_rows_bf16(p.B, dst, p.N, p.K, kp, s)) != hipSuccess) return e;
             p.B = dst;

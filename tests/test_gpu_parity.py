@@ -535,17 +535,20 @@ def test_full_size_sampled(workload, gemm, orders):
         if g.N % 64:
             # backward-data reduces over N, here not a multiple of 64: also force
             # both ring plans (three A tiles and three B tiles), which run the
-            # partial last stage themselves, whatever the tuner picked
+            # partial last stage themselves, and the first with dY, W or both
+            # copied to padded rows (copy bits 1, 2, 3), whatever the tuner picked
             forced = 0
-            for pid in (RING, RING_B):
+            for pid, copy in ((RING, 0), (RING_B, 0), (RING + 16, 1), (RING + 32, 2), (RING + 48, 3)):
                 if F.fc_set_plan(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16, pid) != F.FC_OK:
                     continue
                 desc = F.fc_plan_describe(F.OP_BWD_DATA, g.M, g.K, g.N, xo, wo, F.OUT_BF16)
-                assert desc["ktail"] == g.N % 64 and desc["pad"] == 0 and desc["ws"] == 0, desc
+                assert desc["ktail"] == g.N % 64 and desc["copy"] == copy, desc
+                assert desc["pad"] == (0 if copy == 0 else g.N + 64 - g.N % 64), desc
+                assert (desc["ws"] == 0) == (copy == 0), desc
                 _check_sampled(c, "bwd_data", f"w{workload}g{gemm} bwd_data forced plan={pid} {desc['kernel']} "
-                                              f"ktail={desc['ktail']}", rng)
+                                              f"ktail={desc['ktail']} copy={copy} pad={desc['pad']}", rng)
                 forced += 1
-            assert forced == 2, "a ring plan does not apply"
+            assert forced == 5, "a ring plan does not apply"
         del c
         torch.cuda.empty_cache()
 
