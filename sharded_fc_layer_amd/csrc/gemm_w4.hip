@@ -161,11 +161,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     da.init(wave, lane, g.lda, w.m0, g.M);
     db.init(wave, lane, g.ldb, w.n0, g.N);
 
+    // zeroed by MFMAs once the first stage's loads are on their way (w4_acc_zero)
     f32x4 acc[8][TN];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     bf16x8 fa[2][8], fb[2][TN];
 
     // byte offsets of stage SIDX along the reduction (past the end: the last stage)
@@ -219,6 +216,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
     if (nkt > 0) {
         FCW64_ISSUE(a0, b0, 0)
+        w4_acc_zero(acc);
         FCW64_ISSUE(a1, b1, 1)
         waitcnt<kLoads, 0>();
         __builtin_amdgcn_s_barrier();
@@ -232,6 +230,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             FCW64_STAGE(t + 1, a1, b1, a0, b0)
         }
         waitcnt<0, 0>();  // drain the trailing prefetches
+    } else {
+        w4_acc_zero(acc);
     }
 #undef FCW64_STEPS
 #undef FCW64_ISSUE
