@@ -342,14 +342,25 @@ int default_plan(const Problem& p) {
             break;
         }
     }
-    // 256x256 tiles filling the chip: the one-wave-per-SIMD kernel with
-    // 64-value stages when the reduction allows it, else the 8-wave
-    // ping-pong kernel; otherwise the 4-wave pipelined kernel with the
-    // largest tile that still fills the chip
-    // (a reduction that is not a multiple of 64 would be padded through the
-    // workspace: not for a default plan)
+    // 256x256 tiles filling the chip: the ring kernel when its virtual (zero)
+    // stages add at most 5 % to the reduction, else the two-slot kernel when
+    // the reduction allows it without padding, else the ring if they add at
+    // most 25 %, else the 8-wave ping-pong kernel; otherwise the 4-wave
+    // pipelined kernel with the largest tile that still fills the chip (a
+    // default plan never needs the workspace)
+    const int ring = encode_plan(0, 0, 0, kFamilyW4 + 2);
+    const bool ring_ok = tile == 0 && plan_applies(p, decode_plan(ring)) && ws_layout(p, decode_plan(ring)).total == 0;
+    // the ring's virtual stages: none for a head form (stage count 2 or 4
+    // mod 6 with a whole period after it), else those padding the count to
+    // whole periods (a partial last stage takes one virtual stage's place)
+    const int64_t whole = p.K / 64, stages = (p.K + 63) / 64;
+    const int64_t virt = p.K % 64 != 0 ? 5 - whole % 6
+                         : ((stages % 6 == 2 || stages % 6 == 4) && stages > 6) ? 0
+                                                                               : (6 - stages % 6) % 6;
+    if (ring_ok && virt * 20 <= stages) return ring;
     const int w64 = encode_plan(0, 0, 0, kFamilyW4 + 1);
     if (tile == 0 && plan_applies(p, decode_plan(w64)) && ws_layout(p, decode_plan(w64)).total == 0) return w64;
+    if (ring_ok && virt * 4 <= stages) return ring;
     const int pp = encode_plan(0, 0, 0, 4);  // two-barrier ping-pong, 16x16x32
     if (tile == 0 && plan_applies(p, decode_plan(pp))) return pp;
     const int pipe = encode_plan(tile, 0, 0, 0);
