@@ -112,6 +112,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device copy (a known-size reference for HBM counters)")
     p.add_argument("--no-clock", action="store_true", help="skip the clock pass and the MFMA-only probe")
+    p.add_argument("--force-plan", type=int, default=None,
+                   help="after loading or tuning the plans, run every product with this plan id where it "
+                        "applies (counter runs: the kernels that other tunings pick)")
     p.add_argument("--probe-iters", type=int, default=60000,
                    help="MFMA-only probe: rounds of 64 MFMAs per wave (60000: about 0.5 s)")
     return p.parse_args()
@@ -572,6 +575,10 @@ def main():
         log(f"tuned {len(layers)} shapes in {tune_s:.1f} s")
         if args.plans:
             F.fc_plans_save(args.plans)
+    if args.force_plan is not None:
+        forced = sum(F.fc_set_plan(op, L.g.M, L.g.K, L.g.N, L.xo, L.wo, F.OUT_BF16, args.force_plan) == F.FC_OK
+                     for L in layers for op in (F.OP_FWD, F.OP_BWD_DATA, F.OP_BWD_WEIGHT))
+        log(f"plan {args.force_plan} forced on {forced} of {3 * len(layers)} products")
 
     ms, per_step, wall = run_timed(layers, args.steps, args.warmup, torch)
     flops = step_flops(layers)

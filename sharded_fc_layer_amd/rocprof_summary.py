@@ -184,6 +184,22 @@ def traffic(fetch_db: str, write_db: str, copy_kernel: str, copy_bytes: int, out
     return res
 
 
+def merge_traffic(main: dict, other: dict, label: str) -> dict:
+    """Adds to `main` (traffic()'s result) what `other` measured and it did
+    not: kernels it lacks, and launch grids missing from a kernel it has.
+    A record taken from `other` gets "run": label. Each run's figures stay
+    scaled by that run's own copy calibration."""
+    for k, rec in other["kernels"].items():
+        mine = main["kernels"].get(k)
+        if mine is None:
+            main["kernels"][k] = dict(rec, run=label)
+            continue
+        for g, grec in rec.get("by_grid", {}).items():
+            if g not in mine.setdefault("by_grid", {}):
+                mine["by_grid"][g] = dict(grec, run=label)
+    return main
+
+
 def _bench_line(path: str):
     """The JSON line bench.py printed in a run's log (None if there is none)."""
     import json
@@ -237,10 +253,13 @@ def algorithmic_bytes(bench: dict):
 
 
 def report(out_dir: str, workload: str, number: int, prof: str, source_hash: str, json_path: str = None,
-           copy_kernel: str = "elementwise", copy_bytes: int = 1 << 30):
+           copy_kernel: str = "elementwise", copy_bytes: int = 1 << 30, alt_plans=()):
     """The three summaries of workload `workload` (bench.py --workload
     `number`) from the runs under `prof`, named as the commands in each file's
-    header say."""
+    header say. `alt_plans`: plan ids of further counter-run pairs made with
+    bench.py --force-plan (fetch_w<n>_p<id>, write_w<n>_p<id>); the traffic
+    records take from them the kernels and launch grids that the tuned plans'
+    runs did not launch (another tuning may pick them)."""
     import io
     import json
     import os
@@ -254,6 +273,12 @@ def report(out_dir: str, workload: str, number: int, prof: str, source_hash: str
                  f"--no-clock --copy-calibration --steps 5 --warmup 2",
         "write": f"rocprofv3 --pmc WRITE_SIZE -d {prof} -o write_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra "
                  f"--no-clock --copy-calibration --steps 5 --warmup 2",
+        **{f"fetch_p{i}": f"rocprofv3 --pmc FETCH_SIZE -d {prof} -o fetch_{tag}_p{i} -- {bench_cmd} --no-cpu-baseline "
+                          f"--no-extra --no-clock --copy-calibration --steps 5 --warmup 2 --force-plan {i}"
+           for i in alt_plans},
+        **{f"write_p{i}": f"rocprofv3 --pmc WRITE_SIZE -d {prof} -o write_{tag}_p{i} -- {bench_cmd} --no-cpu-baseline "
+                          f"--no-extra --no-clock --copy-calibration --steps 5 --warmup 2 --force-plan {i}"
+           for i in alt_plans},
         "mfma": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                 f"GRBM_GUI_ACTIVE -d {prof} -o mfma_{tag} -- {bench_cmd} --no-cpu-baseline --no-extra "
                 f"--steps 5 --warmup 2",
@@ -303,14 +328,29 @@ def report(out_dir: str, workload: str, number: int, prof: str, source_hash: str
     buf = io.StringIO()
     tr = traffic(os.path.join(prof, f"fetch_{tag}_results.db"), os.path.join(prof, f"write_{tag}_results.db"),
                  copy_kernel, copy_bytes, buf)
-    lines = header("HBM traffic per launch", ["tune", "fetch", "write"],
+    alt_bufs = []
+    for i in alt_plans:
+        b = io.StringIO()
+        alt = traffic(os.path.join(prof, f"fetch_{tag}_p{i}_results.db"),
+                      os.path.join(prof, f"write_{tag}_p{i}_results.db"), copy_kernel, copy_bytes, b)
+        new_k = sorted(k for k in alt["kernels"] if k not in tr["kernels"])
+        merge_traffic(tr, alt, f"p{i}")
+        alt_bufs.append((i, b.getvalue(), new_k))
+    alt_opt = f" --alt-plans {','.join(str(i) for i in alt_plans)}" if alt_plans else ""
+    alt_keys = [k for i in alt_plans for k in (f"fetch_p{i}", f"write_p{i}")]
+    lines = header("HBM traffic per launch", ["tune", "fetch", "write"] + alt_keys,
                    f"{me} --report profiles --workload {w} --workload-number {number} --prof-dir {prof} "
-                   f"--source-hash {source_hash} --json profiles/traffic.json")
+                   f"--source-hash {source_hash} --json profiles/traffic.json{alt_opt}")
     lines += ["# The copy reference is one torch elementwise kernel (out = in * 1) over 2^29 bf16",
               "# values: it reads and writes exactly 1 GiB. Each counter is scaled by",
               "# (1 GiB / what it read for that copy). FETCH_SIZE counts L2 misses to the data",
               "# fabric (MALL or HBM).", "#"]
     lines += buf.getvalue().rstrip("\n").splitlines()
+    for i, text, new_k in alt_bufs:
+        lines += ["#", f"# counter runs with plan {i} forced where it applies (bench.py --force-plan {i}); the",
+                  "# traffic records take from them the kernels and launch grids the tuned plans did not launch:",
+                  f"# {', '.join(new_k) if new_k else 'no new kernel'}"]
+        lines += text.rstrip("\n").splitlines()
     alg = algorithmic_bytes(trace_bench)
     lines.append("#")
     for k, rec in sorted(tr["kernels"].items()):
@@ -380,10 +420,12 @@ def main():
     ap.add_argument("--report", metavar="DIR", default=None)
     ap.add_argument("--prof-dir", default="gpurun_out/prof")
     ap.add_argument("--workload-number", type=int, default=5)
+    ap.add_argument("--alt-plans", default="", help="comma-separated plan ids of --force-plan counter runs")
     a = ap.parse_args()
     if a.report:
+        alt = [int(x) for x in a.alt_plans.split(",") if x.strip()]
         report(a.report, a.workload, a.workload_number, a.prof_dir, a.source_hash, a.json, a.copy_kernel,
-               a.copy_bytes)
+               a.copy_bytes, alt)
     elif a.traffic:
         res = traffic(a.traffic[0], a.traffic[1], a.copy_kernel, a.copy_bytes)
         if a.json:

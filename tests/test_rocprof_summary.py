@@ -155,3 +155,21 @@ def test_report_refuses_runs_of_another_workload():
         with pytest.raises(ValueError, match="timed workload 'mlp_up_shard_h12288_2x2x2'"):
             R.report(d, "gpt_block_h2048_t8192", 2, d, "0" * 16)
         assert sorted(os.listdir(d)) == ["trace_w2.log"]
+
+
+def test_forced_plan_runs_add_only_what_the_tuned_runs_lack():
+    """Counter runs with another plan forced fill in the kernels (and launch
+    grids) the tuned plans' runs did not launch; what those runs measured stays."""
+    main = {"kernels": {"k1": {"launches": 2, "hbm_bytes_per_launch": 10.0,
+                               "by_grid": {"64": {"launches": 2, "hbm_bytes_per_launch": 10.0}}}}}
+    alt = {"kernels": {"k1": {"launches": 3, "hbm_bytes_per_launch": 99.0,
+                              "by_grid": {"64": {"launches": 1, "hbm_bytes_per_launch": 98.0},
+                                          "128": {"launches": 2, "hbm_bytes_per_launch": 30.0}}},
+                       "k2": {"launches": 1, "hbm_bytes_per_launch": 7.0,
+                              "by_grid": {"32": {"launches": 1, "hbm_bytes_per_launch": 7.0}}}}}
+    R.merge_traffic(main, alt, "p576")
+    k1, k2 = main["kernels"]["k1"], main["kernels"]["k2"]
+    assert k1["hbm_bytes_per_launch"] == 10.0 and k1["by_grid"]["64"]["hbm_bytes_per_launch"] == 10.0
+    assert k1["by_grid"]["128"] == {"launches": 2, "hbm_bytes_per_launch": 30.0, "run": "p576"}
+    assert "run" not in k1 and "run" not in k1["by_grid"]["64"]
+    assert k2["run"] == "p576" and k2["hbm_bytes_per_launch"] == 7.0
