@@ -418,7 +418,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--source-hash", default=None)
     ap.add_argument("--report", metavar="DIR", default=None)
-    ap.add_argument("--prof-dir", default="gpurun_out/prof")
+    ap.add_argument("--prof-dir", default="prof", help="directory of the rocprofv3 runs (-d of their commands)")
     ap.add_argument("--workload-number", type=int, default=5)
     ap.add_argument("--alt-plans", default="", help="comma-separated plan ids of --force-plan counter runs")
     a = ap.parse_args()
